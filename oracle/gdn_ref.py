@@ -1,0 +1,245 @@
+"""CPU oracle for the gated delta-rule (GDN) prefill and decode paths.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module:
+only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may call it.  It shares no code with the HIP library.
+
+Everything is evaluated token by token in float64, the plain definition of the
+recurrence with no chunking, blocking or reordering.  The inputs are the exact
+values the device receives (bf16 inputs already widened), so the only
+difference from the device is arithmetic precision and evaluation order.
+
+The recurrence (the gated delta rule of Yang, Kautz & Hatamizadeh, "Gated Delta
+Networks: Improving Mamba2 with Delta Rule", ICLR 2025), per value head, with an
+fp32 state S of shape [Dk, Dv]:
+
+    S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+    o_t = scale * S_t^T q_t
+
+The pages ("GDN CTE Kernel API Reference", "GDN TKG Kernel API Reference",
+"GDN Block TKG Kernel API Reference") fix the interfaces, layouts, the GQA head
+map and the operators around the core.  Readings taken where they are silent
+are listed next to each function.
+
+Pinned by tests/test_oracle_pins.py (brute force, closed forms, invariants and
+library routines), not by retyping these formulas.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["bf16_round", "l2norm", "sigmoid", "softplus", "silu",
+           "rms_norm_gated", "cte", "tkg", "conv1d_decode", "in_proj",
+           "block_tkg", "L2_EPS", "RMS_EPS"]
+
+#: epsilon inside the l2 norm: x / sqrt(sum(x^2) + L2_EPS).  The TKG page names
+#: "l2norm(q,k)" without a formula; this is the plain reading.
+L2_EPS = 1e-6
+#: default epsilon of RMSNormGated (the TKG page gives none; passed explicitly).
+RMS_EPS = 1e-6
+
+
+# --------------------------------------------------------------------------
+# scalar helpers
+# --------------------------------------------------------------------------
+def bf16_round(x):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits.  With x = m * 2**e, 0.5 <= |m| < 1,
+    the result is round(m * 2**8) * 2**(e - 8) with numpy's half-to-even
+    rounding.  Only the normal range is handled (no overflow or subnormals),
+    which covers every value these tests produce.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def l2norm(x, eps=L2_EPS):
+    """x / sqrt(sum(x^2) + eps) over the last axis ("l2norm(q,k)", TKG page,
+    summary line)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def sigmoid(x):
+    """1 / (1 + exp(-x)) ("beta=sigmoid(b)", TKG page, summary line)."""
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+
+
+def softplus(x):
+    """log(1 + exp(x)), evaluated without overflow as logaddexp(0, x)
+    ("softplus(a+dt_bias)", TKG page, summary line).  No threshold is applied."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def rms_norm_gated(o, z, weight, eps=RMS_EPS):
+    """RMSNormGated(out, z) (TKG page, summary line; parameters z, norm_weight).
+
+    Reading: normalise o by the root mean square over the value axis of one
+    head, multiply by the weight (gamma) directly, then gate with silu(z):
+        y = weight * o / sqrt(mean(o^2) + eps) * silu(z)
+    """
+    o = np.asarray(o, dtype=np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return np.asarray(weight, np.float64) * (o / np.sqrt(ms + eps)) * silu(z)
+
+
+# --------------------------------------------------------------------------
+# prefill (GDN CTE Kernel API Reference, gdn_cte)
+# --------------------------------------------------------------------------
+def cte(query, key, value, g_log, beta, scale=1.0, initial_state=None):
+    """Token-by-token gdn_cte.
+
+    query, key: [B, Hk, S, Dk] (token-major, already unit length: the page's
+    Notes require it and the oracle does not renormalise); value: [B, Hv, S, Dv];
+    g_log, beta: [B, Hv, S]; initial_state: [B, Hv, Dk, Dv] or None (zero state,
+    "parameter recurrent_state").  Value head h reads key/query head
+    h // (Hv // Hk) (page Notes, GQA).
+
+    Returns out [B, Hv, S, Dv] (un-normalised, "return" of gdn_cte) and the
+    final state [B, Hv, Dk, Dv].
+
+    Readings: the output uses the updated state S_t; the delta uses the decayed
+    state (it follows from exp(g)(I - beta k k^T) S); scale multiplies q.
+    """
+    query = np.asarray(query, np.float64)
+    key = np.asarray(key, np.float64)
+    value = np.asarray(value, np.float64)
+    g_log = np.asarray(g_log, np.float64)
+    beta = np.asarray(beta, np.float64)
+    B, Hk, S, Dk = query.shape
+    Hv, Dv = value.shape[1], value.shape[3]
+    assert Hv % Hk == 0
+    kv_head = np.arange(Hv) // (Hv // Hk)
+
+    if initial_state is None:
+        St = np.zeros((B, Hv, Dk, Dv))
+    else:
+        St = np.array(initial_state, dtype=np.float64, copy=True)
+    out = np.empty((B, Hv, S, Dv))
+    for t in range(S):
+        k = key[:, kv_head, t]                      # [B, Hv, Dk]
+        q = query[:, kv_head, t]
+        v = value[:, :, t]                          # [B, Hv, Dv]
+        a = np.exp(g_log[:, :, t])[..., None, None]
+        b = beta[:, :, t][..., None, None]
+        # (I - b k k^T) S  ==  S - b k (k^T S)
+        kS = np.einsum("bhk,bhkv->bhv", k, St)
+        St = a * (St - b * k[..., :, None] * kS[..., None, :]) \
+            + b * k[..., :, None] * v[..., None, :]
+        out[:, :, t] = scale * np.einsum("bhkv,bhk->bhv", St, q)
+    return out, St
+
+
+# --------------------------------------------------------------------------
+# decode step (GDN TKG Kernel API Reference, gdn_tkg)
+# --------------------------------------------------------------------------
+def tkg(q, k, v, b, a, A_log, dt_bias, z, norm_weight, state_in, num_v_heads,
+        rms_eps=RMS_EPS):
+    """One fused decode step for BH = B * num_v_heads independent heads.
+
+    q, k: [BH, K] raw (not normalised); v, z: [BH, V]; b, a: [BH];
+    A_log, dt_bias: [num_v_heads], indexed by bh % num_v_heads (heads cycle
+    fastest per batch, page Dimensions); norm_weight: [V]; state_in [BH, K, V].
+
+    Prologue (page summary and Notes): q^ = l2norm(q) / sqrt(K) (the 1/sqrt(K)
+    query scale is applied after the norm), k^ = l2norm(k), beta = sigmoid(b),
+    g = -exp(A_log) * softplus(a + dt_bias).  Core: one step of the recurrence,
+    written here with the explicit transition matrix
+    Phi = exp(g) (I - beta k^ k^T).  Epilogue: RMSNormGated(o, z), rounded to
+    bf16 ("return": bf16 output).
+
+    Returns (y [BH, V] as float64 holding bf16 values, state [BH, K, V]).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S0 = np.asarray(state_in, np.float64)
+    BH, K = q.shape
+    head = np.arange(BH) % num_v_heads
+
+    qn = l2norm(q) / np.sqrt(K)
+    kn = l2norm(k)
+    beta = sigmoid(b)
+    g = -np.exp(np.asarray(A_log, np.float64)[head]) * softplus(
+        np.asarray(a, np.float64) + np.asarray(dt_bias, np.float64)[head])
+
+    eye = np.eye(K)
+    Phi = np.exp(g)[:, None, None] * (
+        eye - beta[:, None, None] * kn[:, :, None] * kn[:, None, :])
+    S1 = Phi @ S0 + beta[:, None, None] * kn[:, :, None] * v[:, None, :]
+    o = np.einsum("nkv,nk->nv", S1, qn)
+    y = bf16_round(rms_norm_gated(o, z, norm_weight, rms_eps))
+    return y, S1
+
+
+# --------------------------------------------------------------------------
+# fused decode layer (GDN Block TKG Kernel API Reference, gdn_block_tkg)
+# --------------------------------------------------------------------------
+def in_proj(hidden, W):
+    """hidden [B, H] times W [H, N] (W == nn.Linear.weight.T, page parameters),
+    accumulated exactly in float64 and rounded to bf16 (reading: bf16
+    activations at every stage boundary)."""
+    return bf16_round(np.asarray(hidden, np.float64) @ np.asarray(W, np.float64))
+
+
+def conv1d_decode(x_new, conv_state, conv_weight):
+    """Depthwise causal conv1d decode ("conv + silu + slide-window state",
+    Block TKG page summary).
+
+    x_new [B, C] (bf16 values), conv_state [B, C, K_win] (bf16 values, oldest
+    first), conv_weight [C, K_win].  Reading: the window drops its oldest
+    slot and appends the new input; tap K_win-1 multiplies the newest input;
+    no bias.  Returns (silu(sum_j w[c,j] * window[b,c,j]) in float64,
+    new window).
+    """
+    window = np.concatenate(
+        [np.asarray(conv_state, np.float64)[:, :, 1:],
+         np.asarray(x_new, np.float64)[:, :, None]], axis=2)
+    acc = np.sum(window * np.asarray(conv_weight, np.float64)[None], axis=2)
+    return silu(acc), window
+
+
+def block_tkg(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_state,
+              A_log, dt_bias, norm_weight, recurrent_state, num_k_heads,
+              num_v_heads, head_k_dim, head_v_dim, rms_eps=RMS_EPS):
+    """gdn_block_tkg: in_proj -> conv1d decode -> split q|k|v + GQA repeat ->
+    gdn_tkg -> [B, 1, value_dim].  Functional (page Notes): returns
+    (out, conv_state', recurrent_state').
+
+    Readings: q|k|v are packed as contiguous blocks [q (key_dim) | k (key_dim) |
+    v (value_dim)]; the conv output is rounded to bf16 before the decode step
+    (the bf16 window stores the same stage's input); a and b are the bf16
+    projections widened for the gate math; the output is bf16.
+    """
+    hidden = np.asarray(hidden, np.float64)
+    B = hidden.shape[0]
+    x = hidden.reshape(B, -1)
+    Hk, Hv, Dk, Dv = num_k_heads, num_v_heads, head_k_dim, head_v_dim
+    key_dim = Hk * Dk
+
+    mixed = in_proj(x, W_in_qkv)
+    zz = in_proj(x, W_in_z)
+    aa = in_proj(x, W_in_a)
+    bb = in_proj(x, W_in_b)
+    conv_out, new_window = conv1d_decode(mixed, conv_state, conv_weight)
+    conv_out = bf16_round(conv_out)
+
+    q = conv_out[:, :key_dim].reshape(B, Hk, Dk)
+    k = conv_out[:, key_dim:2 * key_dim].reshape(B, Hk, Dk)
+    v = conv_out[:, 2 * key_dim:].reshape(B, Hv, Dv)
+    kv_head = np.arange(Hv) // (Hv // Hk)
+    q = q[:, kv_head].reshape(B * Hv, Dk)
+    k = k[:, kv_head].reshape(B * Hv, Dk)
+
+    y, S1 = tkg(q, k, v.reshape(B * Hv, Dv), bb.reshape(B * Hv), aa.reshape(B * Hv),
+                A_log, dt_bias, zz.reshape(B * Hv, Dv), norm_weight,
+                np.asarray(recurrent_state, np.float64).reshape(B * Hv, Dk, Dv),
+                Hv, rms_eps)
+    return y.reshape(B, 1, Hv * Dv), new_window, S1.reshape(B, Hv, Dk, Dv)

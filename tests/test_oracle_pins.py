@@ -1,0 +1,463 @@
+"""Pins for the CPU oracle (both the numpy version and its plain-C twin).
+
+Each test ties the oracle to something other than itself: a hand-worked
+example, a brute-force evaluation in mpmath of the unrolled transition
+products, closed forms at special points, invariants the recurrence must obey,
+and a library triangular solve of the chunk (WY) form.  They run on the CPU.
+"""
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.linalg
+
+from gated_delta_rule_cte_amd import inputs
+from oracle import c_ref, gdn_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *nums = line.split()
+            vals[key] = np.array([float(x) for x in nums])
+    return vals
+
+
+CTE_IMPLS = {"numpy": gdn_ref.cte, "c": c_ref.cte}
+
+
+def _tkg_c(*args, rms_eps=gdn_ref.RMS_EPS):
+    y, s = c_ref.tkg_unrounded(*args, rms_eps=rms_eps)
+    return gdn_ref.bf16_round(y), s
+
+
+TKG_IMPLS = {"numpy": gdn_ref.tkg, "c": _tkg_c}
+
+
+def _rand_cte(rng, B, Hk, Hv, S, Dk, Dv, g=(-0.5, -0.01), state=True):
+    q = rng.standard_normal((B, Hk, S, Dk))
+    k = rng.standard_normal((B, Hk, S, Dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, Hv, S, Dv))
+    gl = rng.uniform(g[0], g[1], (B, Hv, S))
+    be = rng.uniform(0.05, 0.95, (B, Hv, S))
+    s0 = 0.1 * rng.standard_normal((B, Hv, Dk, Dv)) if state else None
+    return q, k, v, gl, be, s0
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_hand_worked_example(impl):
+    gv = _read_golden("cte_worked_example.txt")
+    q = np.stack([gv["q1"], gv["q2"]])[None, None]
+    k = np.stack([gv["k1"], gv["k2"]])[None, None]
+    v = np.stack([gv["v1"], gv["v2"]])[None, None]
+    g = np.array([gv["g1"][0], gv["g2"][0]])[None, None]
+    b = np.array([gv["beta1"][0], gv["beta2"][0]])[None, None]
+    out, st = CTE_IMPLS[impl](q, k, v, g, b, 1.0, None)
+    np.testing.assert_allclose(out[0, 0, 0], gv["o1"], atol=1e-14)
+    np.testing.assert_allclose(out[0, 0, 1], gv["o2"], atol=1e-14)
+    np.testing.assert_allclose(st[0, 0], np.stack([gv["S2_row0"], gv["S2_row1"]]), atol=1e-14)
+
+
+def _mp_bruteforce(q, k, v, g, b, scale, s0):
+    """mpmath, 50 digits: S_t = Phi_t...Phi_1 S0 + sum_i Phi_t...Phi_{i+1} b_i k_i v_i^T
+    with Phi_i = exp(g_i)(I - b_i k_i k_i^T); o_t = scale S_t^T q_t.  One head."""
+    mpmath.mp.dps = 50
+    S, Dk = q.shape
+    Dv = v.shape[1]
+    M = mpmath.matrix
+    I = mpmath.eye(Dk)
+    col = lambda x: M([[mpmath.mpf(float(t))] for t in x])
+    Phi = []
+    for i in range(S):
+        kk = col(k[i])
+        Phi.append(mpmath.exp(mpmath.mpf(float(g[i]))) * (I - mpmath.mpf(float(b[i])) * kk * kk.T))
+    S0 = M([[mpmath.mpf(float(x)) for x in row] for row in s0])
+    outs, St = [], None
+    for t in range(S):
+        prod = I
+        for i in range(t, -1, -1):
+            prod = prod * Phi[i]
+        St = prod * S0
+        for i in range(t + 1):
+            tail = I
+            for j in range(t, i, -1):
+                tail = tail * Phi[j]
+            St += tail * (mpmath.mpf(float(b[i])) * col(k[i]) * col(v[i]).T)
+        o = mpmath.mpf(float(scale)) * St.T * col(q[t])
+        outs.append([float(o[j]) for j in range(Dv)])
+    return np.array(outs), np.array([[float(St[i, j]) for j in range(Dv)] for i in range(Dk)])
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+@pytest.mark.parametrize("Dk,Dv,S", [(1, 1, 5), (2, 3, 4), (3, 2, 6), (3, 3, 3)])
+def test_cte_mpmath_bruteforce(impl, Dk, Dv, S):
+    rng = np.random.default_rng(100 + 10 * Dk + Dv)
+    q, k, v, g, b, s0 = _rand_cte(rng, 1, 1, 2, S, Dk, Dv)
+    out, st = CTE_IMPLS[impl](q, k, v, g, b, 0.7, s0)
+    for h in range(2):
+        ref_o, ref_s = _mp_bruteforce(q[0, 0], k[0, 0], v[0, h], g[0, h], b[0, h], 0.7, s0[0, h])
+        np.testing.assert_allclose(out[0, h], ref_o, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(st[0, h], ref_s, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_beta_zero_is_pure_decay(impl):
+    rng = np.random.default_rng(7)
+    q, k, v, g, b, s0 = _rand_cte(rng, 2, 1, 2, 40, 8, 6)
+    b[:] = 0.0
+    out, st = CTE_IMPLS[impl](q, k, v, g, b, 0.3, s0)
+    gam = np.cumsum(g, axis=-1)                            # [B,Hv,S]
+    np.testing.assert_allclose(st, np.exp(gam[..., -1])[..., None, None] * s0, rtol=1e-13)
+    ref = 0.3 * np.exp(gam)[..., None] * np.einsum("bhkv,bsk->bhsv", s0, q[:, 0])
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_write_is_exact_for_orthonormal_keys(impl):
+    """g = 0, beta = 1, orthonormal keys: every write is exact, S^T k_j = v_j, and
+    directions orthogonal to all keys keep the initial response."""
+    rng = np.random.default_rng(8)
+    Dk, Dv, n = 8, 5, 6
+    basis, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    keys = basis[:, :n].T                                   # n orthonormal rows
+    q = keys[None, None].copy()                             # q_t = k_t
+    k = keys[None, None].copy()
+    v = rng.standard_normal((1, 1, n, Dv))
+    g = np.zeros((1, 1, n))
+    b = np.ones((1, 1, n))
+    s0 = rng.standard_normal((1, 1, Dk, Dv))
+    out, st = CTE_IMPLS[impl](q, k, v, g, b, 0.5, s0)
+    np.testing.assert_allclose(out[0, 0], 0.5 * v[0, 0], atol=1e-13)
+    np.testing.assert_allclose(keys @ st[0, 0], v[0, 0], atol=1e-13)
+    for j in range(n, Dk):
+        np.testing.assert_allclose(basis[:, j] @ st[0, 0], basis[:, j] @ s0[0, 0], atol=1e-13)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_chaining_equals_single_call(impl):
+    rng = np.random.default_rng(9)
+    q, k, v, g, b, s0 = _rand_cte(rng, 2, 2, 4, 50, 6, 7)
+    o_all, s_all = CTE_IMPLS[impl](q, k, v, g, b, 0.4, s0)
+    o1, s1 = CTE_IMPLS[impl](q[:, :, :23], k[:, :, :23], v[:, :, :23], g[..., :23], b[..., :23], 0.4, s0)
+    o2, s2 = CTE_IMPLS[impl](q[:, :, 23:], k[:, :, 23:], v[:, :, 23:], g[..., 23:], b[..., 23:], 0.4, s1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o_all, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s2, s_all, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_scalar_geometric_closed_form(impl):
+    """Dk = Dv = 1, k = 1, constant g, beta, v: s_t = rho^t s0 + beta v (1-rho^t)/(1-rho)
+    with rho = exp(g)(1 - beta); o_t = scale q s_t."""
+    S, g0, b0, v0, s00, q0 = 30, -0.2, 0.3, 1.7, -0.4, 0.9
+    q = np.full((1, 1, S, 1), q0)
+    k = np.ones((1, 1, S, 1))
+    v = np.full((1, 1, S, 1), v0)
+    g = np.full((1, 1, S), g0)
+    b = np.full((1, 1, S), b0)
+    out, st = CTE_IMPLS[impl](q, k, v, g, b, 0.25, np.full((1, 1, 1, 1), s00))
+    rho = math.exp(g0) * (1 - b0)
+    t = np.arange(1, S + 1)
+    s_t = rho ** t * s00 + b0 * v0 * (1 - rho ** t) / (1 - rho)
+    np.testing.assert_allclose(out[0, 0, :, 0], 0.25 * q0 * s_t, rtol=1e-13)
+    np.testing.assert_allclose(st[0, 0, 0, 0], s_t[-1], rtol=1e-13)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_linear_in_values_and_state(impl):
+    rng = np.random.default_rng(10)
+    q, k, v, g, b, s0 = _rand_cte(rng, 1, 1, 2, 20, 5, 4)
+    v2 = rng.standard_normal(v.shape)
+    s02 = rng.standard_normal(s0.shape)
+    f = lambda vv, ss: CTE_IMPLS[impl](q, k, vv, g, b, 0.6, ss)
+    oa, sa = f(v, s0)
+    ob, sb = f(v2, s02)
+    oc, sc = f(2.0 * v - 3.0 * v2, 2.0 * s0 - 3.0 * s02)
+    np.testing.assert_allclose(oc, 2 * oa - 3 * ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sc, 2 * sa - 3 * sb, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_gqa_equals_explicit_repeat(impl):
+    rng = np.random.default_rng(11)
+    q, k, v, g, b, s0 = _rand_cte(rng, 2, 2, 6, 12, 4, 3)
+    o1, s1 = CTE_IMPLS[impl](q, k, v, g, b, 0.5, s0)
+    rep = [h // 3 for h in range(6)]                     # value head h reads key head h // 3
+    o2, s2 = CTE_IMPLS[impl](q[:, rep], k[:, rep], v, g, b, 0.5, s0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+@pytest.mark.parametrize("S", [1, 17, 64])
+def test_cte_single_chunk_wy_form_via_triangular_solve(impl, S):
+    """One chunk in the WY (chunk-parallel) form with scipy's unit-lower triangular
+    solve equals the token recurrence:
+      A[t,i] = beta_t (k_t.k_i) e^{gam_t-gam_i} (i<t);  (I+A) U = beta*V - beta*Gam*(K H)
+      O = scale (Gam*(Q H) + (Q K^T . M) U),  M[t,i] = e^{gam_t-gam_i} (i<=t)
+      H' = Gam_S H + (e^{gam_S-gam} * K)^T U"""
+    rng = np.random.default_rng(12 + S)
+    Dk, Dv = 16, 8
+    q, k, v, g, b, s0 = _rand_cte(rng, 1, 1, 1, S, Dk, Dv)
+    o, st = CTE_IMPLS[impl](q, k, v, g, b, 0.8, s0)
+    Q, K, Vv, gg, bb, H = q[0, 0], k[0, 0], v[0, 0], g[0, 0], b[0, 0], s0[0, 0]
+    gam = np.cumsum(gg)
+    D = np.exp(gam[:, None] - gam[None, :])
+    A = np.tril(bb[:, None] * (K @ K.T) * D, -1)
+    rhs = bb[:, None] * Vv - (bb * np.exp(gam))[:, None] * (K @ H)
+    U = scipy.linalg.solve_triangular(np.eye(S) + A, rhs, lower=True, unit_diagonal=True)
+    O = 0.8 * (np.exp(gam)[:, None] * (Q @ H) + np.tril((Q @ K.T) * D) @ U)
+    Hn = np.exp(gam[-1]) * H + (np.exp(gam[-1] - gam)[:, None] * K).T @ U
+    np.testing.assert_allclose(o[0, 0], O, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0], Hn, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("impl", CTE_IMPLS)
+def test_cte_state_norm_bound(impl):
+    """||I - beta k k^T||_2 <= 1 for unit k and beta in (0,1), so
+    ||S_t||_2 <= e^{g_t} ||S_{t-1}||_2 + beta_t ||v_t||; checked on prefixes."""
+    rng = np.random.default_rng(13)
+    q, k, v, g, b, s0 = _rand_cte(rng, 1, 1, 1, 25, 6, 5)
+    prev = np.linalg.norm(s0[0, 0], 2)
+    for t in range(1, 26):
+        _, st = CTE_IMPLS[impl](q[:, :, :t], k[:, :, :t], v[:, :, :t], g[..., :t], b[..., :t], 1.0, s0)
+        cur = np.linalg.norm(st[0, 0], 2)
+        assert cur <= math.exp(g[0, 0, t - 1]) * prev + b[0, 0, t - 1] * np.linalg.norm(v[0, 0, t - 1]) + 1e-12
+        prev = cur
+
+
+def test_cte_c_twin_matches_numpy():
+    rng = np.random.default_rng(14)
+    q, k, v, g, b, s0 = _rand_cte(rng, 2, 2, 4, 33, 16, 8)
+    o1, s1 = gdn_ref.cte(q, k, v, g, b, 0.25, s0)
+    o2, s2 = c_ref.cte(q, k, v, g, b, 0.25, s0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-14)
+    o3, s3 = c_ref.cte(q, k, v, g, b, 0.25, None)
+    o4, s4 = gdn_ref.cte(q, k, v, g, b, 0.25, np.zeros_like(s0))
+    np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s3, s4, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+def test_scalar_helpers_closed_forms():
+    assert gdn_ref.sigmoid(0.0) == 0.5
+    assert abs(gdn_ref.softplus(0.0) - math.log(2)) < 1e-16
+    assert abs(gdn_ref.softplus(50.0) - 50.0) < 1e-15
+    assert abs(gdn_ref.softplus(-50.0) - math.exp(-50.0)) < 1e-30
+    np.testing.assert_allclose(gdn_ref.l2norm(np.array([3.0, 4.0, 0.0]), eps=0.0), [0.6, 0.8, 0.0])
+    assert gdn_ref.silu(0.0) == 0.0
+    assert abs(gdn_ref.silu(40.0) - 40.0) < 1e-15
+
+
+def test_bf16_round_known_values_and_generator_agreement():
+    r = gdn_ref.bf16_round
+    assert r(1.0 + 2.0 ** -8) == 1.0                        # tie -> even (1.0)
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6       # tie -> even mantissa
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert r(-3.0) == -3.0 and r(0.0) == 0.0
+    x = np.random.default_rng(15).standard_normal(10000).astype(np.float32)
+    np.testing.assert_array_equal(r(x.astype(np.float64)), inputs.bf16(x).f64())
+
+
+@pytest.mark.parametrize("impl", TKG_IMPLS)
+def test_tkg_hand_worked_example(impl):
+    gv = _read_golden("tkg_worked_example.txt")
+    y, s1 = TKG_IMPLS[impl](gv["q"][None], gv["k"][None], gv["v"][None], gv["b"], gv["a"],
+                            gv["A_log"], gv["dt_bias"], gv["z"][None], gv["norm_weight"],
+                            np.stack([gv["S0_row0"], gv["S0_row1"]])[None], 1)
+    np.testing.assert_allclose(s1[0], np.stack([gv["S1_row0"], gv["S1_row1"]]), atol=1e-14)
+    np.testing.assert_allclose(y[0], gv["y"], rtol=2.0 ** -8)
+    np.testing.assert_array_equal(y[0], gdn_ref.bf16_round(y[0]))
+
+
+@pytest.mark.parametrize("impl", TKG_IMPLS)
+def test_tkg_gate_and_head_indexing(impl):
+    """beta ~ 0 (b = -60) leaves only the decay: S' = exp(g) S0 with
+    g = -exp(A_log[h]) softplus(a + dt_bias[h]) and h = bh % num_v_heads."""
+    rng = np.random.default_rng(16)
+    Hv, B, K, V = 3, 2, 8, 4
+    A_log = np.log(np.array([1.0, 2.0, 3.0]))
+    dt_bias = np.array([0.0, 0.5, -0.5])
+    a = rng.uniform(-1, 1, B * Hv)
+    s0 = rng.standard_normal((B * Hv, K, V))
+    y, s1 = TKG_IMPLS[impl](rng.standard_normal((B * Hv, K)), rng.standard_normal((B * Hv, K)),
+                            rng.standard_normal((B * Hv, V)), np.full(B * Hv, -60.0), a,
+                            A_log, dt_bias, rng.standard_normal((B * Hv, V)), np.ones(V), s0, Hv)
+    for n in range(B * Hv):
+        h = n % Hv
+        alpha = math.exp(-(h + 1) * math.log1p(math.exp(a[n] + dt_bias[h])))
+        np.testing.assert_allclose(s1[n], alpha * s0[n], rtol=1e-12)
+
+
+@pytest.mark.parametrize("impl", TKG_IMPLS)
+def test_tkg_constant_output_closed_form(impl):
+    """Zero state and q = k: S' = beta k^ v^T and o = beta (k^.q^) v.  With v = c*1
+    the output is constant across V, so RMSNormGated gives the closed form
+    y = sign(c') (1 + eps/c'^2)^(-1/2) w * silu(z), c' = beta c (k^.q^)."""
+    rng = np.random.default_rng(17)
+    K, V, c = 16, 8, 0.003
+    qk = rng.standard_normal((1, K))
+    z = rng.standard_normal((1, V))
+    w = rng.uniform(0.5, 1.5, V)
+    y, _ = TKG_IMPLS[impl](qk, qk, np.full((1, V), c), np.array([0.4]), np.array([0.1]),
+                           np.array([0.0]), np.array([0.0]), z, w, np.zeros((1, K, V)), 1)
+    beta = 1 / (1 + math.exp(-0.4))
+    nrm2 = float(np.sum(qk * qk))
+    kq = nrm2 / (nrm2 + 1e-6) / math.sqrt(K)
+    cp = beta * c * kq
+    ref = np.sign(cp) / math.sqrt(1 + 1e-6 / cp ** 2) * w * z[0] / (1 + np.exp(-z[0]))
+    np.testing.assert_allclose(y[0], ref, rtol=2.0 ** -8)
+
+
+def test_rms_norm_gated_properties():
+    rng = np.random.default_rng(18)
+    o = rng.standard_normal((4, 16))
+    w = rng.standard_normal(16)
+    assert np.all(gdn_ref.rms_norm_gated(o, np.zeros((4, 16)), w) == 0.0)
+    z = rng.standard_normal((4, 16))
+    np.testing.assert_allclose(gdn_ref.rms_norm_gated(7.5 * o, z, w, eps=0.0),
+                               gdn_ref.rms_norm_gated(o, z, w, eps=0.0), rtol=1e-13)
+    # unit rms rows pass through as w * o * silu(z) when eps = 0
+    u = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    np.testing.assert_allclose(gdn_ref.rms_norm_gated(u, z, w, eps=0.0), w * u * z / (1 + np.exp(-z)),
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("impl", TKG_IMPLS)
+def test_decode_step_equals_one_token_prefill(impl):
+    rng = np.random.default_rng(19)
+    Hv, B, K, V = 4, 3, 16, 8
+    BH = B * Hv
+    q, k = rng.standard_normal((BH, K)), rng.standard_normal((BH, K))
+    v, z = rng.standard_normal((BH, V)), rng.standard_normal((BH, V))
+    b, a = rng.standard_normal(BH), rng.standard_normal(BH)
+    A_log, dt_bias = np.log(rng.uniform(1, 16, Hv)), rng.uniform(-1, 1, Hv)
+    w = 1 + 0.1 * rng.standard_normal(V)
+    s0 = 0.05 * rng.standard_normal((BH, K, V))
+    y, s1 = TKG_IMPLS[impl](q, k, v, b, a, A_log, dt_bias, z, w, s0, Hv)
+    h = np.arange(BH) % Hv
+    g = -np.exp(A_log[h]) * np.log1p(np.exp(a + dt_bias[h]))
+    beta = 1 / (1 + np.exp(-b))
+    qn = q / np.sqrt(np.sum(q * q, -1, keepdims=True) + 1e-6)
+    kn = k / np.sqrt(np.sum(k * k, -1, keepdims=True) + 1e-6)
+    sh = lambda x: x.reshape(B, Hv, 1, -1)
+    o, st = CTE_IMPLS[impl](sh(qn), sh(kn), sh(v), g.reshape(B, Hv, 1), beta.reshape(B, Hv, 1),
+                            1 / math.sqrt(K), s0.reshape(B, Hv, K, V))
+    np.testing.assert_allclose(s1, st.reshape(BH, K, V), rtol=1e-12, atol=1e-15)
+    o = o.reshape(BH, V)
+    rms = np.sqrt(np.mean(o * o, -1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(y, gdn_ref.bf16_round(w * o / rms * z / (1 + np.exp(-z))),
+                               rtol=2.0 ** -7, atol=0)
+
+
+def test_tkg_c_twin_matches_numpy():
+    d = inputs.tkg_inputs(2, 4, 32, 16, seed=20)
+    args = [d[n].f64() for n in ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "state_in")]
+    y1, s1 = gdn_ref.tkg(*args, 4)
+    y2, s2 = _tkg_c(*args, 4)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=1e-15)
+    assert np.max(np.abs(y1 - y2)) <= 2.0 ** -7 * np.max(np.abs(y1))
+
+
+# ---------------------------------------------------------------------------
+# fused decode layer
+# ---------------------------------------------------------------------------
+def test_conv1d_decode_one_hot_and_correlate():
+    rng = np.random.default_rng(21)
+    B, C, W = 2, 5, 4
+    st = gdn_ref.bf16_round(rng.standard_normal((B, C, W)))
+    x = gdn_ref.bf16_round(rng.standard_normal((B, C)))
+    for j in range(W):
+        w = np.zeros((C, W))
+        w[:, j] = 1.0
+        out, win = gdn_ref.conv1d_decode(x, st, w)
+        full = np.concatenate([st, x[:, :, None]], axis=2)       # oldest .. newest
+        np.testing.assert_array_equal(win, full[:, :, 1:])
+        np.testing.assert_allclose(out, gdn_ref.silu(full[:, :, 1 + j]), rtol=1e-15)
+    w = rng.standard_normal((C, W))
+    out, _ = gdn_ref.conv1d_decode(x, st, w)
+    full = np.concatenate([st, x[:, :, None]], axis=2)
+    for bb in range(B):
+        for c in range(C):
+            ref = np.correlate(full[bb, c], w[c], mode="valid")[-1]   # newest window
+            assert abs(out[bb, c] - gdn_ref.silu(ref)) < 1e-13
+
+
+def test_conv1d_decode_window_after_k_steps_holds_last_inputs():
+    rng = np.random.default_rng(22)
+    B, C, W = 1, 3, 4
+    st = rng.standard_normal((B, C, W))
+    xs = rng.standard_normal((W, B, C))
+    for t in range(W):
+        _, st = gdn_ref.conv1d_decode(xs[t], st, np.ones((C, W)))
+    np.testing.assert_array_equal(st, np.moveaxis(xs, 0, 2))
+
+
+def test_in_proj_selection_matrix_is_exact():
+    rng = np.random.default_rng(23)
+    h = gdn_ref.bf16_round(rng.standard_normal((3, 10)))
+    sel = np.zeros((10, 7))
+    pick = rng.integers(0, 10, 7)
+    sel[pick, np.arange(7)] = 1.0
+    np.testing.assert_array_equal(gdn_ref.in_proj(h, sel), h[:, pick])
+
+
+def test_block_wiring_split_and_gqa():
+    """Selection-matrix projections and a newest-tap conv make q|k|v, z, a, b known
+    functions of the hidden vector; the block must equal the decode step on those
+    explicitly gathered operands (packing q|k|v, GQA map h // (Hv/Hk), BH order)."""
+    rng = np.random.default_rng(24)
+    B, Hk, Hv, Dk, Dv, W = 2, 2, 4, 4, 3, 4
+    key_dim, value_dim = Hk * Dk, Hv * Dv
+    conv_dim = 2 * key_dim + value_dim
+    H = conv_dim + value_dim + 2 * Hv
+    hidden = gdn_ref.bf16_round(rng.standard_normal((B, 1, H)))
+
+    def sel(off, n):
+        m = np.zeros((H, n))
+        m[off + np.arange(n), np.arange(n)] = 1.0
+        return m
+    Wqkv, Wz = sel(0, conv_dim), sel(conv_dim, value_dim)
+    Wa, Wb = sel(conv_dim + value_dim, Hv), sel(conv_dim + value_dim + Hv, Hv)
+    conv_w = np.zeros((conv_dim, W))
+    conv_w[:, W - 1] = 1.0
+    conv_state = gdn_ref.bf16_round(rng.standard_normal((B, conv_dim, W)))
+    A_log, dt_bias = np.log(rng.uniform(1, 16, Hv)), rng.uniform(-1, 1, Hv)
+    w = 1 + 0.1 * rng.standard_normal(Dv)
+    S0 = 0.05 * rng.standard_normal((B, Hv, Dk, Dv))
+    y, cs, st = gdn_ref.block_tkg(hidden, Wqkv, Wz, Wa, Wb, conv_w, conv_state, A_log, dt_bias,
+                                  w, S0, Hk, Hv, Dk, Dv)
+    x = hidden[:, 0]
+    act = gdn_ref.bf16_round(gdn_ref.silu(x[:, :conv_dim]))
+    qs, ks, vs, zs, as_, bs, ss = [], [], [], [], [], [], []
+    for bb in range(B):
+        for h in range(Hv):
+            hk = h // (Hv // Hk)
+            qs.append(act[bb, hk * Dk:(hk + 1) * Dk])
+            ks.append(act[bb, key_dim + hk * Dk:key_dim + (hk + 1) * Dk])
+            vs.append(act[bb, 2 * key_dim + h * Dv:2 * key_dim + (h + 1) * Dv])
+            zs.append(x[bb, conv_dim + h * Dv:conv_dim + (h + 1) * Dv])
+            as_.append(x[bb, conv_dim + value_dim + h])
+            bs.append(x[bb, conv_dim + value_dim + Hv + h])
+            ss.append(S0[bb, h])
+    y2, s2 = gdn_ref.tkg(np.array(qs), np.array(ks), np.array(vs), np.array(bs), np.array(as_),
+                         A_log, dt_bias, np.array(zs), w, np.array(ss), Hv)
+    np.testing.assert_array_equal(y[:, 0], y2.reshape(B, value_dim))
+    np.testing.assert_array_equal(st, s2.reshape(B, Hv, Dk, Dv))
+    np.testing.assert_array_equal(cs[:, :, -1], x[:, :conv_dim])
+    np.testing.assert_array_equal(cs[:, :, :-1], conv_state[:, :, 1:])
