@@ -1,0 +1,71 @@
+"""Build libgdn.so (hand-written HIP for gfx950) in-tree with hipcc.
+
+    python -m gated_delta_rule_cte_amd.build
+
+Each translation unit is compiled to an object under ``_build/`` in parallel,
+then linked into ``gated_delta_rule_cte_amd/libgdn.so``.  Always recompiles.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgdn.so")
+SOURCES = ["gdn_api.cpp", "gdn_tkg.hip", "gdn_cte.hip", "gdn_block.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; libgdn needs ROCm to build")
+    return exe
+
+
+def compile_flags(extra=()):
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # no packed-fp32 instructions are generated anywhere in the library
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-I", CSRC, *extra]
+
+
+def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+
+    def one(src):
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [cc, *compile_flags(extra_flags), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                         if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+        if msgs.strip() and verbose:
+            print(msgs, flush=True)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

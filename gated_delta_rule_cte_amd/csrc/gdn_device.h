@@ -1,0 +1,110 @@
+// Device-side helpers shared by the libgdn kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf2f(__bf16 b) { return static_cast<float>(b); }
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ __bf16 f2bf(float f) { return static_cast<__bf16>(f); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return f2bf(x); }
+
+// ---------------------------------------------------------------------------
+// 8-element vectors: the per-lane operand slice of one 16x32 MFMA fragment,
+// and the unit of global <-> LDS copies (16 B of bf16, 32 B of fp32).
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> {
+  uint4 u;
+  __device__ __forceinline__ static Vec8 zero() { Vec8 v; v.u = make_uint4(0, 0, 0, 0); return v; }
+  __device__ __forceinline__ static Vec8 load(const __bf16* p) { Vec8 v; v.u = *reinterpret_cast<const uint4*>(p); return v; }
+  __device__ __forceinline__ void store(__bf16* p) const { *reinterpret_cast<uint4*>(p) = u; }
+  __device__ __forceinline__ float get(int j) const {
+    const uint32_t w = (&u.x)[j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  __device__ __forceinline__ bf16x8 frag() const { return __builtin_bit_cast(bf16x8, u); }
+};
+template <> struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ static Vec8 zero() { Vec8 v; v.a = make_float4(0, 0, 0, 0); v.b = v.a; return v; }
+  __device__ __forceinline__ static Vec8 load(const float* p) {
+    Vec8 v; v.a = reinterpret_cast<const float4*>(p)[0]; v.b = reinterpret_cast<const float4*>(p)[1]; return v;
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    reinterpret_cast<float4*>(p)[0] = a; reinterpret_cast<float4*>(p)[1] = b;
+  }
+  __device__ __forceinline__ float get(int j) const { return j < 4 ? (&a.x)[j] : (&b.x)[j - 4]; }
+};
+
+// ---------------------------------------------------------------------------
+// 16x16 output, K = 32 per call.  Fragment convention (both operands): lane l
+// supplies row/col (l % 16) and the 8 contraction indices 8*(l/16) .. +7.
+// Accumulator: lane l holds D[4*(l/16) + i][l % 16], i = 0..3.
+// bf16 uses v_mfma_f32_16x16x32_bf16; fp32 issues eight v_mfma_f32_16x16x4_f32,
+// instruction s pairing contraction index 8*(l/16) + s of both operands.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+  __device__ __forceinline__ static f4 mma(const Vec8<__bf16>& a, const Vec8<__bf16>& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.frag(), b.frag(), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  __device__ __forceinline__ static f4 mma(const Vec8<float>& a, const Vec8<float>& b, f4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, c, 0, 0, 0);
+    return c;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront reductions / scans (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// log(1 + e^x); above 20 the correction e^-x is below fp32 resolution of x.
+__device__ __forceinline__ float softplusf_(float x) { return x > 20.0f ? x : log1pf(__expf(x)); }
+
+}  // namespace gdn

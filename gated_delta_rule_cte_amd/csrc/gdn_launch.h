@@ -1,0 +1,74 @@
+// Internal launch interface between the C-ABI layer (gdn_api.cpp) and the
+// kernels.  Arguments are validated before any of these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// ---------------------------------------------------------------- decode step
+struct TkgParams {
+  // q/k row of head bh = b * Hv + h starts at base + b * qk_bstride + (h / head_div) * K
+  const void* q;
+  const void* k;
+  long qk_bstride;
+  int head_div;
+  // v row: v + b * v_bstride + h * V ; z row: z + bh * V
+  const void* v;
+  long v_bstride;
+  const void* z;
+  const float* b;
+  const float* a;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_weight;
+  const float* state_in;
+  float* state_out;
+  void* out;  // bf16 [BH, V]
+  int BH, Hv, K, V;
+  float rms_eps;
+};
+// dtype: 0 fp32, 1 bf16 (q, k, v, z)
+hipError_t launch_tkg(const TkgParams& p, int dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+struct CteParams {
+  const void* q;    // [B, Hk, S, Dk]
+  const void* k;
+  const void* v;    // [B, Hv, S, Dv]
+  const float* g;   // [B, Hv, S]
+  const float* beta;
+  float* state;     // [B, Hv, Dk, Dv]
+  void* out;        // [B, Hv, S, Dv]
+  int B, Hk, Hv, S, Dk, Dv;
+  int has_initial_state;
+  float scale;
+};
+hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode layer
+struct BlockParams {
+  const void* hidden;      // [B, H] bf16
+  const void* W_qkv;       // [H, conv_dim] bf16
+  const void* W_z;         // [H, value_dim]
+  const void* W_a;         // [H, Hv]
+  const void* W_b;         // [H, Hv]
+  const float* conv_weight;  // [conv_dim, K_win]
+  const void* conv_state_in;  // [B, conv_dim, K_win] bf16
+  void* conv_state_out;
+  // workspace slices
+  void* ws_conv_out;  // [B, conv_dim] bf16
+  void* ws_z;         // [B, value_dim] bf16
+  float* ws_a;        // [B, Hv]
+  float* ws_b;        // [B, Hv]
+  int B, H, Hk, Hv, Dk, Dv, K_win;
+};
+struct BlockWorkspace {
+  size_t conv_out, z, a, b, total;  // byte offsets and total size
+};
+BlockWorkspace block_workspace_layout(int B, int Hk, int Hv, int Dk, int Dv);
+hipError_t launch_block_proj(const BlockParams& p, hipStream_t stream);
+
+}  // namespace gdn

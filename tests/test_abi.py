@@ -1,0 +1,166 @@
+"""C-ABI contract tests that need no GPU: libgdn loads, exports every symbol
+include/gdn.h declares, and rejects bad arguments with the documented status
+before any HIP call (fake, never-dereferenced device addresses are passed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_cte_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+A = 0x10000000      # fake 16-byte aligned addresses, far apart
+STEP = 0x10000000
+
+
+def addrs(n):
+    return [ctypes.c_void_p(A + i * STEP) for i in range(n)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built (run python -m gated_delta_rule_cte_amd.build)")
+    return gdn.load()
+
+
+def test_header_declarations_match_exports(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^(?:int|size_t|const char\*)\s+(gdn_\w+)\(", text, re.M))
+    assert declared == set(gdn.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_version() == 100
+    for code, name in gdn.STATUS.items():
+        assert lib.gdn_status_string(code).decode() == name
+    assert lib.gdn_status_string(-99).decode() == "GDN_ERR_UNKNOWN"
+
+
+def cte_call(lib, **kw):
+    args = dict(B=1, Hk=2, Hv=4, S=128, Dk=64, Dv=64, dtype=gdn.GDN_BF16, algorithm=0,
+                has_init=1)
+    args.update(kw)
+    p = addrs(7)
+    ptrs = kw.get("ptrs", p)
+    return lib.gdn_cte(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], 0.125, ptrs[5], args["has_init"],
+                       ptrs[6], args["B"], args["Hk"], args["Hv"], args["S"], args["Dk"], args["Dv"],
+                       args["dtype"], args["algorithm"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), -3),
+    (dict(algorithm=1), -7),
+    (dict(Hv=3), -2),
+    (dict(Hk=0), -2),
+    (dict(Dk=130), -2),
+    (dict(Dv=12), -2),
+    (dict(Dk=0), -2),
+    (dict(S=-1), -2),
+    (dict(B=-2), -2),
+])
+def test_cte_rejects_bad_shapes(lib, kw, status):
+    assert cte_call(lib, **kw) == status
+    assert lib.gdn_last_error().decode() != ""
+
+
+def test_cte_rejects_null_misaligned_and_aliased(lib):
+    p = addrs(7)
+    bad = list(p)
+    bad[2] = None
+    assert cte_call(lib, ptrs=bad) == -1
+    bad = list(p)
+    bad[0] = ctypes.c_void_p(A + 8)
+    assert cte_call(lib, ptrs=bad) == -4
+    bad = list(p)
+    bad[6] = ctypes.c_void_p(p[2].value + 64)       # out inside value
+    assert cte_call(lib, ptrs=bad) == -5
+    bad = list(p)
+    bad[5] = ctypes.c_void_p(p[3].value)            # state on top of g_log
+    assert cte_call(lib, ptrs=bad) == -5
+
+
+def test_cte_valid_call_without_gpu_reports_device(lib):
+    # every argument check passes; the device check is last
+    assert cte_call(lib) == -9
+    assert "device" in lib.gdn_last_error().decode().lower()
+
+
+def test_cte_empty_batch_is_a_no_op(lib):
+    assert cte_call(lib, B=0) == 0
+    assert lib.gdn_last_error().decode() == ""
+
+
+def tkg_call(lib, ptrs=None, BH=64, Hv=32, K=128, V=128, dtype=gdn.GDN_BF16, eps=1e-6):
+    p = ptrs or addrs(12)
+    return lib.gdn_tkg(*p, BH, Hv, K, V, dtype, eps, None)
+
+
+def test_tkg_checks(lib):
+    assert tkg_call(lib, Hv=5) == -2
+    assert tkg_call(lib, K=136) == -2
+    assert tkg_call(lib, V=4) == -2
+    assert tkg_call(lib, dtype=3) == -3
+    assert tkg_call(lib, eps=-1.0) == -2
+    assert tkg_call(lib, BH=0) == 0
+    p = addrs(12)
+    q = list(p)
+    q[10] = p[9]                                     # state_out == state_in: allowed
+    assert tkg_call(lib, ptrs=q) == -9
+    q = list(p)
+    q[10] = ctypes.c_void_p(p[9].value + 4096)       # partial overlap: rejected
+    assert tkg_call(lib, ptrs=q) == -5
+    q = list(p)
+    q[11] = ctypes.c_void_p(p[3].value)              # out on top of v
+    assert tkg_call(lib, ptrs=q) == -5
+    q = list(p)
+    q[0] = None
+    assert tkg_call(lib, ptrs=q) == -1
+    assert tkg_call(lib) == -9
+
+
+def block_call(lib, ptrs=None, ws=None, ws_bytes=None, **kw):
+    d = dict(B=64, H=2048, Hk=16, Hv=32, Dk=128, Dv=128, K_win=4)
+    d.update(kw)
+    need = lib.gdn_block_tkg_workspace_size(d["B"], d["H"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], d["K_win"])
+    p = ptrs or addrs(14)
+    ws = ctypes.c_void_p(A + 20 * STEP) if ws is None else ws
+    return lib.gdn_block_tkg(*p, d["B"], d["H"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], d["K_win"], 1e-6,
+                             ws, need if ws_bytes is None else ws_bytes, None)
+
+
+def test_block_checks(lib):
+    need = lib.gdn_block_tkg_workspace_size(64, 2048, 16, 32, 128, 128, 4)
+    conv_dim = 2 * 16 * 128 + 32 * 128
+    assert need >= 64 * conv_dim * 2 + 64 * 4096 * 2 + 2 * 64 * 32 * 4
+    assert block_call(lib, H=2000) == -2
+    assert block_call(lib, Hv=24) == -2
+    assert block_call(lib, K_win=9) == -2
+    assert block_call(lib, Dk=120) == -9              # 120 is a multiple of 8: accepted
+    assert block_call(lib, ws_bytes=need - 1) == -6
+    assert block_call(lib, ws=ctypes.c_void_p(0), ws_bytes=need) == -6
+    assert block_call(lib, B=0) == 0
+    p = addrs(14)
+    q = list(p)
+    q[12] = p[6]                                     # conv_state_out == conv_state_in: allowed
+    q[13] = p[10]                                    # recurrent_state_out == in: allowed
+    assert block_call(lib, ptrs=q) == -9
+    q = list(p)
+    q[11] = ctypes.c_void_p(p[0].value)              # out on top of hidden
+    assert block_call(lib, ptrs=q) == -5
+    assert block_call(lib) == -9
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = gdn._lib
+    try:
+        gdn._lib = None
+        with pytest.raises(ImportError):
+            gdn.load(str(tmp_path / "missing.so"))
+    finally:
+        gdn._lib = saved

@@ -1,0 +1,285 @@
+"""GPU parity: every libgdn entry point, called through the C ABI (via the thin
+binding), against the fp64 CPU oracle on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_cte_amd import inputs
+from oracle import c_ref, gdn_ref
+from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def _run_cte(gdn, d, with_state):
+    st = dev(d["recurrent_state"]).clone() if with_state else None
+    out, state = gdn.gdn_cte(dev(d["query"]), dev(d["key"]), dev(d["value"]), dev(d["g_log"]),
+                             dev(d["beta"]), d["scale"], recurrent_state=st)
+    _sync()
+    return host(out), host(state)
+
+
+def _oracle_cte(d, with_state, heads=None):
+    """C-twin oracle; `heads` = list of (b, h) to evaluate (None = all)."""
+    q, k, v = d["query"].f64(), d["key"].f64(), d["value"].f64()
+    g, be = d["g_log"].f64(), d["beta"].f64()
+    s0 = d["recurrent_state"].f64() if with_state else None
+    if heads is None:
+        return c_ref.cte(q, k, v, g, be, d["scale"], s0)
+    # gather the sampled heads into one batch-1 call (key head per value head)
+    Hk, Hv = q.shape[1], v.shape[1]
+    kv = [h // (Hv // Hk) for _, h in heads]
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    ro, rs = c_ref.cte(q[bs, kv][None], k[bs, kv][None], v[bs, hs][None], g[bs, hs][None],
+                       be[bs, hs][None], d["scale"], None if s0 is None else s0[bs, hs][None])
+    return {bh: (ro[:, i:i + 1], rs[:, i:i + 1]) for i, bh in enumerate(heads)}
+
+
+CTE_CASES = [
+    # (B, Hk, Hv, S, Dk, Dv, dtype, with_state)
+    (1, 2, 2, 128, 64, 64, "f32", False),      # the small fp32 workload's shape
+    (2, 1, 3, 77, 64, 32, "f32", True),        # ragged tail, GQA 1:3, narrow Dv
+    (1, 2, 4, 200, 128, 128, "f32", True),     # DK = 128 fp32 path, several chunks
+    (1, 1, 1, 1, 16, 24, "f32", True),         # one token, tiny odd dims
+    (1, 2, 4, 300, 128, 128, "bf16", True),    # ragged, GQA 1:2, in-place state
+    (2, 2, 2, 64, 40, 72, "bf16", False),      # padded Dk, Dv not a tile multiple
+    (1, 4, 4, 1000, 64, 128, "bf16", True),    # DK = 64 bf16 path
+]
+
+
+@pytest.mark.parametrize("case", CTE_CASES, ids=lambda c: "B{}_Hk{}_Hv{}_S{}_Dk{}_Dv{}_{}_{}".format(
+    *c[:7], "state" if c[7] else "zero"))
+def test_cte_matches_oracle(gpu_lib, case):
+    B, Hk, Hv, S, Dk, Dv, dt, ws = case
+    d = inputs.cte_inputs(B, Hk, Hv, S, Dk, Dv, dtype=dt, g_range=(-0.5, -0.01),
+                          state_std=0.05 if ws else None, seed=1000 + S)
+    o, s = _run_cte(gpu_lib, d, ws)
+    ro, rs = _oracle_cte(d, ws)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(o, ro, tol, 2, "out")
+    assert_close(s, rs, tol, 2, "state")
+
+
+def test_cte_empty_sequence(gpu_lib):
+    import torch
+    d = inputs.cte_inputs(1, 2, 2, 0, 64, 64, dtype="bf16", state_std=0.05, seed=5)
+    init = dev(d["recurrent_state"]).clone()
+    out, st = gpu_lib.gdn_cte(dev(d["query"]), dev(d["key"]), dev(d["value"]), dev(d["g_log"]),
+                              dev(d["beta"]), d["scale"], recurrent_state=init.clone())
+    _sync()
+    assert out.shape == (1, 2, 0, 64)
+    assert torch.equal(st, init)
+    out, st = gpu_lib.gdn_cte(dev(d["query"]), dev(d["key"]), dev(d["value"]), dev(d["g_log"]),
+                              dev(d["beta"]), d["scale"])
+    _sync()
+    assert torch.count_nonzero(st).item() == 0
+
+
+def test_cte_small_fp32_workload(gpu_lib):
+    """B=1, Hk=Hv=2, S=128, Dk=Dv=64, fp32, zero state: element-by-element."""
+    d = inputs.workload_inputs("cte_fp32_b1_h2_s128_d64")
+    o, s = _run_cte(gpu_lib, d, False)
+    ro, rs = gdn_ref.cte(d["query"].f64(), d["key"].f64(), d["value"].f64(), d["g_log"].f64(),
+                         d["beta"].f64(), d["scale"], None)
+    assert_close(o, ro, TOL_F32, 2, "out")
+    assert_close(s, rs, TOL_F32, 2, "state")
+
+
+def test_cte_gqa_s4096_workload(gpu_lib):
+    """B=1, Hk=16, Hv=32, S=4096, D=128, bf16, supplied state updated in place:
+    every head against the oracle."""
+    d = inputs.workload_inputs("cte_bf16_b1_hk16_hv32_s4096_d128")
+    o, s = _run_cte(gpu_lib, d, True)
+    ro, rs = _oracle_cte(d, True)
+    assert_close(o, ro, TOL_BF16, 2, "out")
+    assert_close(s, rs, TOL_BF16, 2, "state")
+
+
+def test_cte_long_batched_workload_and_chaining(gpu_lib):
+    """B=4, Hk=16, Hv=32, S=16384, D=128, bf16, zero state: sampled heads against
+    the oracle; four chained S=4096 calls carrying the state equal the single call."""
+    import torch
+    d = inputs.workload_inputs("cte_bf16_b4_hk16_hv32_s16384_d128")
+    q, k, v = dev(d["query"]), dev(d["key"]), dev(d["value"])
+    g, be = dev(d["g_log"]), dev(d["beta"])
+    out, st = gpu_lib.gdn_cte(q, k, v, g, be, d["scale"])
+    _sync()
+    heads = [(0, 0), (1, 7), (2, 16), (3, 31), (3, 1), (0, 30)]
+    ref = _oracle_cte(d, False, heads)
+    o_h, s_h = host(out), host(st)
+    for (b, h), (ro, rs) in ref.items():
+        assert_close(o_h[b:b + 1, h:h + 1], ro, TOL_BF16, 2, f"out head {(b, h)}")
+        assert_close(s_h[b:b + 1, h:h + 1], rs, TOL_BF16, 2, f"state head {(b, h)}")
+    # chained: 4 x 4096 with the state carried
+    state = None
+    outs = []
+    for c in range(4):
+        sl = slice(4096 * c, 4096 * (c + 1))
+        oc, state = gpu_lib.gdn_cte(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(),
+                                    v[:, :, sl].contiguous(), g[:, :, sl].contiguous(),
+                                    be[:, :, sl].contiguous(), d["scale"], recurrent_state=state)
+        outs.append(oc)
+    _sync()
+    assert torch.equal(torch.cat(outs, dim=2), out), "chained outputs differ from the single call"
+    assert torch.equal(state, st), "chained final state differs from the single call"
+
+
+def test_cte_is_deterministic(gpu_lib):
+    import torch
+    d = inputs.cte_inputs(1, 2, 4, 500, 128, 128, dtype="bf16", state_std=0.05, seed=77)
+    a = _run_cte(gpu_lib, d, True)
+    b = _run_cte(gpu_lib, d, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_cte_special_cases_on_gpu(gpu_lib):
+    """beta = 0 is pure decay: state = exp(sum g) S0 exactly up to fp32 rounding."""
+    import torch
+    d = inputs.cte_inputs(1, 1, 2, 256, 64, 64, dtype="f32", state_std=0.05, seed=78)
+    d["beta"] = inputs.f32(np.zeros_like(d["beta"].data))
+    o, s = _run_cte(gpu_lib, d, True)
+    gam = np.cumsum(d["g_log"].f64(), axis=-1)
+    ref_s = np.exp(gam[..., -1])[..., None, None] * d["recurrent_state"].f64()
+    assert_close(s, ref_s, TOL_F32, 2, "pure-decay state")
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+def _tkg_args(d):
+    return [d[n] for n in ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "state_in")]
+
+
+def _oracle_tkg(d, rms_eps=1e-6):
+    y, s = c_ref.tkg_unrounded(*[x.f64() for x in _tkg_args(d)], d["num_v_heads"], rms_eps=rms_eps)
+    return gdn_ref.bf16_round(y), s
+
+
+TKG_CASES = [
+    # (B, Hv, K, V, dtype)
+    (3, 4, 64, 32, "bf16"),
+    (2, 5, 128, 128, "f32"),
+    (1, 2, 40, 72, "bf16"),
+    (4, 1, 8, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", TKG_CASES, ids=lambda c: "B{}_Hv{}_K{}_V{}_{}".format(*c))
+def test_tkg_matches_oracle(gpu_lib, case):
+    B, Hv, K, V, dt = case
+    d = inputs.tkg_inputs(B, Hv, K, V, dtype=dt, seed=2000 + K + V)
+    y, s = gpu_lib.gdn_tkg(*[dev(x) for x in _tkg_args(d)])
+    _sync()
+    ry, rs = _oracle_tkg(d)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(host(s), rs, tol, 1, "state")
+    assert_close(host(y), ry, TOL_BF16, 1, "out")
+
+
+def test_tkg_bh1024_workload_in_place(gpu_lib):
+    """B=32, Hv=32 (BH=1024), K=V=128, bf16 q/k/v/z: out-of-place and in-place."""
+    import torch
+    d = inputs.workload_inputs("tkg_b32_hv32_d128")
+    args = [dev(x) for x in _tkg_args(d)]
+    y, s = gpu_lib.gdn_tkg(*args)
+    _sync()
+    ry, rs = _oracle_tkg(d)
+    assert_close(host(s), rs, TOL_BF16, 1, "state")
+    assert_close(host(y), ry, TOL_BF16, 1, "out")
+    st = args[-1].clone()
+    y2, s2 = gpu_lib.gdn_tkg(*args[:-1], st, state_out=st)
+    _sync()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(s2, s) and torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-5])
+def test_tkg_rms_eps_sweep(gpu_lib, eps):
+    d = inputs.tkg_inputs(2, 8, 128, 128, seed=2100)
+    y, _ = gpu_lib.gdn_tkg(*[dev(x) for x in _tkg_args(d)], rms_eps=eps)
+    _sync()
+    ry, _ = _oracle_tkg(d, rms_eps=eps)
+    assert_close(host(y), ry, TOL_BF16, 1, f"out eps={eps}")
+
+
+def test_decode_after_prefill(gpu_lib):
+    """Prefill S tokens, then one decode step from the returned state, equals the
+    oracle run the same way (state hand-off between the two entry points)."""
+    import torch
+    B, Hk, Hv, S, D = 1, 2, 4, 192, 128
+    d = inputs.cte_inputs(B, Hk, Hv, S, D, D, dtype="bf16", state_std=0.05, seed=2200)
+    _, st = gpu_lib.gdn_cte(dev(d["query"]), dev(d["key"]), dev(d["value"]), dev(d["g_log"]),
+                            dev(d["beta"]), d["scale"], recurrent_state=dev(d["recurrent_state"]).clone())
+    t = inputs.tkg_inputs(B, Hv, D, D, seed=2201)
+    y, s1 = gpu_lib.gdn_tkg(*[dev(x) for x in _tkg_args(t)[:-1]], st.reshape(B * Hv, D, D).contiguous())
+    _sync()
+    _, rs = c_ref.cte(d["query"].f64(), d["key"].f64(), d["value"].f64(), d["g_log"].f64(),
+                      d["beta"].f64(), d["scale"], d["recurrent_state"].f64())
+    args = [x.f64() for x in _tkg_args(t)[:-1]] + [rs.reshape(B * Hv, D, D)]
+    ry, rs1 = c_ref.tkg_unrounded(*args, Hv)
+    assert_close(host(s1), rs1, TOL_BF16, 1, "state")
+    assert_close(host(y), gdn_ref.bf16_round(ry), TOL_BF16, 1, "out")
+
+
+# ---------------------------------------------------------------------------
+# fused decode layer
+# ---------------------------------------------------------------------------
+BLOCK_KEYS = ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight", "conv_state",
+              "A_log", "dt_bias", "norm_weight", "recurrent_state")
+
+
+def _oracle_block(d):
+    a = [d[n].f64() for n in BLOCK_KEYS]
+    return gdn_ref.block_tkg(*a, d["num_k_heads"], d["num_v_heads"], d["head_k_dim"], d["head_v_dim"])
+
+
+def _check_block(gpu_out, d):
+    y, cs, rs = (host(t) for t in gpu_out)
+    ry, rcs, rrs = _oracle_block(d)
+    B = y.shape[0]
+    Hv, Dv = d["num_v_heads"], d["head_v_dim"]
+    assert_close(rs, rrs, TOL_BF16, 2, "recurrent_state")
+    assert_close(y.reshape(B * Hv, Dv), ry.reshape(B * Hv, Dv), TOL_BF16, 1, "out")
+    # the slid part of the window is copied bit for bit; the new column is the
+    # bf16-rounded projection.  fp32 MFMA accumulation vs fp64 can flip a
+    # rounding (or more, where the sum cancels), so it is held to the per-row
+    # metric and nearly all of it must still be bit-identical.
+    np.testing.assert_array_equal(cs[:, :, :-1], rcs[:, :, :-1])
+    assert_close(cs[:, :, -1], rcs[:, :, -1], TOL_BF16, 1, "conv_state new column")
+    assert np.mean(cs[:, :, -1] == rcs[:, :, -1]) >= 0.99
+
+
+@pytest.mark.parametrize("case", [(3, 256, 2, 4, 32, 32, 4), (5, 384, 1, 2, 64, 48, 3), (2, 128, 2, 2, 16, 16, 1)],
+                         ids=lambda c: "B{}_H{}_Hk{}_Hv{}_Dk{}_Dv{}_W{}".format(*c))
+def test_block_small(gpu_lib, case):
+    B, H, Hk, Hv, Dk, Dv, W = case
+    d = inputs.block_inputs(B, H, Hk, Hv, Dk, Dv, K_win=W, w_std=0.05, seed=3000 + H)
+    out = gpu_lib.gdn_block_tkg(*[dev(d[n]) for n in BLOCK_KEYS])
+    _sync()
+    _check_block(out, d)
+
+
+def test_block_b64_workload_in_place(gpu_lib):
+    """B=64, H=2048, Hk=16, Hv=32, D=128, K_win=4: functional call against the
+    oracle, then the in-place call (caches aliased) gives the same bits."""
+    import torch
+    d = inputs.workload_inputs("block_b64_h2048_hk16_hv32_d128")
+    args = [dev(d[n]) for n in BLOCK_KEYS]
+    out = gpu_lib.gdn_block_tkg(*args)
+    _sync()
+    _check_block(out, d)
+    cs, rs = args[6].clone(), args[10].clone()
+    out2 = gpu_lib.gdn_block_tkg(*args[:6], cs, *args[7:10], rs, conv_state_out=cs, recurrent_state_out=rs)
+    _sync()
+    for a, b in zip(out, out2):
+        assert torch.equal(a, b)
