@@ -129,14 +129,18 @@ const char* gdn_status_string(int status) {
 }
 
 // ------------------------------------------------------------------ gdn_cte
-size_t gdn_cte_workspace_size(int, int, int, int, int, int, int) { return 0; }
+size_t gdn_cte_workspace_size(int B, int Hk, int Hv, int S, int Dk, int Dv, int dtype) {
+  (void)Hk;
+  (void)Dk;
+  (void)Dv;
+  if (B <= 0 || Hv <= 0 || S <= 0 || (dtype != GDN_F32 && dtype != GDN_BF16)) return 0;
+  return gdn::cte_workspace_bytes(B, Hv, S, dtype);
+}
 
 int gdn_cte(const void* query, const void* key, const void* value, const float* g_log,
             const float* beta, float scale, float* recurrent_state, int has_initial_state,
             void* out, int B, int Hk, int Hv, int S, int Dk, int Dv, int dtype, int algorithm,
             void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype %d is not GDN_F32 or GDN_BF16", dtype);
   if (algorithm != GDN_CTE_ALGO_DEFAULT)
     return fail(GDN_ERR_UNSUPPORTED, "algorithm %d is not implemented (only GDN_CTE_ALGO_DEFAULT)", algorithm);
@@ -146,6 +150,9 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
     return fail(GDN_ERR_SHAPE, "Dk=%d, Dv=%d must be multiples of 8 in [8, %d]", Dk, Dv, GDN_MAX_HEAD_DIM);
   if ((long long)B * Hv * ((Dv + 15) / 16) > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "B*Hv too large");
   const size_t es = esize(dtype);
+  // per-head extents are addressed with 32-bit buffer offsets below 2^31
+  if ((size_t)S * 256 * es >= ((size_t)1 << 31))
+    return fail(GDN_ERR_SHAPE, "S=%d is too long for one call (per-head data must stay below 2 GiB)", S);
   const size_t nqk = (size_t)B * Hk * S * Dk * es, nv = (size_t)B * Hv * S * Dv * es;
   const size_t ng = (size_t)B * Hv * S * 4, ns = (size_t)B * Hv * Dk * Dv * 4;
   const Span q{"query", query, nqk}, k{"key", key, nqk}, v{"value", value, nv}, g{"g_log", g_log, ng},
@@ -154,6 +161,16 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
   if (int r = check_disjoint(o, {q, k, v, g, be, st})) return r;
   if (int r = check_disjoint(st, {q, k, v, g, be})) return r;
   if ((size_t)B * Hv == 0) return ok();
+  const size_t need = gdn_cte_workspace_size(B, Hk, Hv, S, Dk, Dv, dtype);
+  if (need > 0) {
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", need);
+    if (workspace_bytes < need)
+      return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    const Span ws{"workspace", workspace, need};
+    if (int r = check_disjoint(ws, {q, k, v, g, be, st, o})) return r;
+  }
   if (int r = check_device()) return r;
   gdn::CteParams p;
   p.q = query; p.k = key; p.v = value; p.g = g_log; p.beta = beta;
@@ -161,6 +178,8 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
   p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
   p.has_initial_state = has_initial_state ? 1 : 0;
   p.scale = scale;
+  p.ws = workspace;
+  p.prof = nullptr;
   return launched(gdn::launch_cte(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -223,6 +242,9 @@ int gdn_block_tkg(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   if (B == 0) return ok();
   const size_t key_dim = (size_t)Hk * Dk, value_dim = (size_t)Hv * Dv;
   const size_t conv_dim = 2 * key_dim + value_dim;
+  // weights and the hidden batch are addressed with 32-bit buffer offsets below 2^31
+  if ((size_t)H * conv_dim * 2 >= ((size_t)1 << 31) || (size_t)B * H * 2 >= ((size_t)1 << 31))
+    return fail(GDN_ERR_SHAPE, "H=%d x conv_dim=%zu weights (or the hidden batch) exceed 2 GiB", H, conv_dim);
   const Span sh{"hidden", hidden, (size_t)B * H * 2}, swq{"W_in_qkv", W_in_qkv, (size_t)H * conv_dim * 2},
       swz{"W_in_z", W_in_z, (size_t)H * value_dim * 2}, swa{"W_in_a", W_in_a, (size_t)H * Hv * 2},
       swb{"W_in_b", W_in_b, (size_t)H * Hv * 2}, scw{"conv_weight", conv_weight, conv_dim * K_win * 4},

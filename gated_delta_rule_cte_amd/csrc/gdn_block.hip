@@ -6,10 +6,12 @@
 //
 // Y[B, N] = hidden[B, H] x [W_in_qkv | W_in_z | W_in_a | W_in_b] is a skinny
 // GEMM (M = batch) that streams each weight byte once, so it is bound by HBM
-// bandwidth.  One workgroup owns 64 output columns of one weight matrix and
-// 64 batch rows and walks H in steps of 128 on bf16 MFMA (16x16x32).  The
-// weight tile arrives N-contiguous and is transposed while it is written to
-// LDS, so both MFMA operands are read as contiguous 16-byte fragments.
+// bandwidth.  One workgroup owns 32 output columns of one weight matrix and
+// 64 batch rows and walks H in steps of 128 on bf16 MFMA (16x16x32), keeping
+// four K tiles of loads in flight in a register ring (branch-free buffer
+// loads).  The weight tile arrives N-contiguous and is transposed two rows at
+// a time (v_perm pairs) while it is written to LDS, so both MFMA operands are
+// read as contiguous 16-byte fragments.
 //
 // Epilogue per output element (b, n), all results rounded to bf16:
 //   q|k|v column c:  window = [state[b,c,1:], y];  act = silu(sum_j w[c,j] window[j])
@@ -24,14 +26,36 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 64;   // batch rows per workgroup
-constexpr int kBN = 64;   // output columns per workgroup
-constexpr int kBK = 128;  // hidden-dimension step
+constexpr int kBM = 64;     // batch rows per workgroup (one 16-row block per wave)
+constexpr int kBN = 32;     // output columns per workgroup
+constexpr int kBK = 128;    // hidden-dimension step
+constexpr int kRing = 4;    // K tiles in flight per workgroup (register ring)
 constexpr int kLD = kBK + 8;
 
-__global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams p) {
-  __shared__ __align__(16) __bf16 sH[kBM * kLD];
-  __shared__ __align__(16) __bf16 sWt[kBN * kLD];
+// weight pair items per thread per K tile: (kBK/2 row pairs) x (kBN/8 column groups)
+constexpr int kWItems = (kBK / 2) * (kBN / 8) / kThreads;
+// hidden items per thread per K tile: kBM rows x (kBK/8) column groups
+constexpr int kHItems = kBM * (kBK / 8) / kThreads;
+static_assert(kWItems == 1 && kHItems * kThreads == kBM * (kBK / 8), "tile split");
+
+struct Ring {
+  Vec8<__bf16> w0, w1;           // weight rows k, k+1 at 8 columns
+  Vec8<__bf16> b0, b1;           // the same from W_in_b (a|b tile only)
+  Vec8<__bf16> hd[kHItems];      // hidden tile slice
+};
+
+// Tile kinds, each its own instantiation so that every buffer descriptor is
+// provably wave-uniform (a per-lane base would turn each load into a loop
+// over distinct descriptors) and the streaming path never conditionally
+// overwrites its load registers (which would make the compiler wait on them):
+//   kSingle   columns of W_in_qkv or W_in_z
+//   kAB       the a|b tile, Hv % 8 == 0: W_in_a and W_in_b each through their
+//             own descriptor, the other one's lanes out of range (zero), OR-ed
+//   kABScalar the a|b tile, Hv % 8 != 0: element by element
+enum { kSingle = 0, kAB = 1, kABScalar = 2 };
+
+template <int kKind>
+__device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH, __bf16* sWt) {
 
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid & (kWave - 1), lr = lane & 15, lg = lane >> 4;
@@ -39,79 +63,131 @@ __global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams 
   const int conv_dim = 2 * key_dim + value_dim;
   const int nt_qkv = (conv_dim + kBN - 1) / kBN;
   const int nt_z = (value_dim + kBN - 1) / kBN;
+  const int H = p.H, B = p.B;
+  const int nkt = H / kBK;
 
+  // column tile -> (matrix, first column); the a|b tile reads W_in_a then W_in_b
   int tile = blockIdx.x, seg, ncols;
-  const __bf16* W;
   if (tile < nt_qkv) {
-    seg = 0; ncols = conv_dim; W = static_cast<const __bf16*>(p.W_qkv);
+    seg = 0; ncols = conv_dim;
   } else if ((tile -= nt_qkv) < nt_z) {
-    seg = 1; ncols = value_dim; W = static_cast<const __bf16*>(p.W_z);
+    seg = 1; ncols = value_dim;
   } else {
-    tile -= nt_z; seg = 2; ncols = 2 * p.Hv; W = nullptr;
+    tile -= nt_z; seg = 2; ncols = 2 * p.Hv;
   }
   const int n0 = tile * kBN;
   const int m0 = blockIdx.y * kBM;
-  const int H = p.H, B = p.B;
-  const __bf16* hid = static_cast<const __bf16*>(p.hidden);
+
+  // Branch-free loads: each element's buffer offset is loop invariant except
+  // for the K-tile step, and masked-off elements (columns past the matrix,
+  // batch rows past B, K tiles past H) fall outside the descriptor range.
+  // Weight item: rows kp, kp+1 (kp = 2 * (tid / 4)), columns n8..n8+7.
+  const int kp = 2 * (tid / (kBN / 8)), n8 = 8 * (tid % (kBN / 8));
+  const int n = n0 + n8;
+  // uniform per workgroup: the matrix this tile reads (the a|b tile: W_in_a)
+  const __bf16* Wbase = seg == 0 ? static_cast<const __bf16*>(p.W_qkv)
+                      : seg == 1 ? static_cast<const __bf16*>(p.W_z)
+                                 : static_cast<const __bf16*>(p.W_a);
+  const int wstride = seg == 0 ? conv_dim : seg == 1 ? value_dim : p.Hv;
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wbase, (uint32_t)((size_t)H * wstride * 2));
+  const uint32_t wrow = (uint32_t)wstride * 2u;
+  const uint32_t wstep = (uint32_t)kBK * wrow;  // bytes per K tile
+  // per lane: kSingle / kAB read column n of W (kAB: of W_in_a when n < Hv),
+  // kAB reads W_in_b's column n - Hv through rWb
+  const bool in_a = kKind == kSingle ? n < ncols : n < p.Hv;
+  const uint32_t wvo = (kKind != kABScalar && in_a) ? ((uint32_t)kp * wrow + (uint32_t)n * 2u) : kOOB;
+  const __amdgpu_buffer_rsrc_t rWb = make_rsrc(p.W_b, (uint32_t)((size_t)H * p.Hv * 2));
+  const uint32_t wvob =
+      (kKind == kAB && n >= p.Hv && n < ncols) ? ((uint32_t)kp * wrow + (uint32_t)(n - p.Hv) * 2u) : kOOB;
+
+  const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.hidden, (uint32_t)((size_t)B * H * 2));
+  uint32_t hvo[kHItems];
+#pragma unroll
+  for (int i = 0; i < kHItems; ++i) {
+    const int it = tid + kThreads * i, m = it / (kBK / 8), k8 = (it % (kBK / 8)) * 8;
+    hvo[i] = (m0 + m < B) ? (uint32_t)((m0 + m) * H + k8) * 2u : kOOB;
+  }
+
+  auto load = [&](Ring& rg, int kt) {
+    // K tiles past the end read zero (their offsets exceed the range)
+    const uint32_t wo = (kt < nkt && wvo != kOOB) ? wvo + (uint32_t)kt * wstep : kOOB;
+    rg.w0 = Vec8<__bf16>::bload(rW, wo);
+    rg.w1 = Vec8<__bf16>::bload(rW, wo == kOOB ? kOOB : wo + wrow);
+    if (kKind == kAB) {
+      const uint32_t wob = (kt < nkt && wvob != kOOB) ? wvob + (uint32_t)kt * wstep : kOOB;
+      rg.b0 = Vec8<__bf16>::bload(rWb, wob);
+      rg.b1 = Vec8<__bf16>::bload(rWb, wob == kOOB ? kOOB : wob + wrow);
+    }
+    if (kKind == kABScalar && kt < nkt) {
+      const uint16_t* Wa = static_cast<const uint16_t*>(p.W_a);
+      const uint16_t* Wb = static_cast<const uint16_t*>(p.W_b);
+      uint16_t e0[8], e1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int cc = n + j;
+        const size_t r0 = (size_t)(kt * kBK + kp) * p.Hv, r1 = r0 + p.Hv;
+        e0[j] = cc < p.Hv ? Wa[r0 + cc] : (cc < 2 * p.Hv ? Wb[r0 + cc - p.Hv] : (uint16_t)0);
+        e1[j] = cc < p.Hv ? Wa[r1 + cc] : (cc < 2 * p.Hv ? Wb[r1 + cc - p.Hv] : (uint16_t)0);
+      }
+      rg.w0.u = make_uint4(e0[0] | (uint32_t)e0[1] << 16, e0[2] | (uint32_t)e0[3] << 16,
+                           e0[4] | (uint32_t)e0[5] << 16, e0[6] | (uint32_t)e0[7] << 16);
+      rg.w1.u = make_uint4(e1[0] | (uint32_t)e1[1] << 16, e1[2] | (uint32_t)e1[3] << 16,
+                           e1[4] | (uint32_t)e1[5] << 16, e1[6] | (uint32_t)e1[7] << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kHItems; ++i)
+      rg.hd[i] = Vec8<__bf16>::bload(rH, (kt < nkt && hvo[i] != kOOB) ? hvo[i] + (uint32_t)kt * kBK * 2u : kOOB);
+  };
 
   f4 acc[kBN / 16];
 #pragma unroll
   for (int nb = 0; nb < kBN / 16; ++nb) acc[nb] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < H; k0 += kBK) {
-    // hidden tile [64 rows][128 k]
-    for (int it = tid; it < kBM * (kBK / 8); it += kThreads) {
-      const int m = it / (kBK / 8), k8 = (it % (kBK / 8)) * 8;
-      const Vec8<__bf16> v = (m0 + m < B) ? Vec8<__bf16>::load(hid + (size_t)(m0 + m) * H + k0 + k8)
-                                          : Vec8<__bf16>::zero();
-      v.store(sH + m * kLD + k8);
-    }
-    // weight tile [128 k][64 n] -> transposed [64 n][128 k]
-    for (int it = tid; it < kBK * (kBN / 8); it += kThreads) {
-      const int k = it / (kBN / 8), n8 = (it % (kBN / 8)) * 8;
-      const int n = n0 + n8;
-      uint16_t e[8];
-      if (seg < 2) {
-        if (n < ncols) {
-          const uint4 u = *reinterpret_cast<const uint4*>(W + (size_t)(k0 + k) * ncols + n);
-          e[0] = u.x & 0xFFFF; e[1] = u.x >> 16; e[2] = u.y & 0xFFFF; e[3] = u.y >> 16;
-          e[4] = u.z & 0xFFFF; e[5] = u.z >> 16; e[6] = u.w & 0xFFFF; e[7] = u.w >> 16;
-        } else {
+  Ring ring[kRing];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) e[j] = 0;
+  for (int u = 0; u < kRing; ++u) load(ring[u], u);
+
+  for (int kt0 = 0; kt0 < nkt; kt0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int kt = kt0 + u;
+      // stage tile kt: hidden rows as is, weight rows transposed in pairs
+#pragma unroll
+      for (int i = 0; i < kHItems; ++i) {
+        const int it = tid + kThreads * i, m = it / (kBK / 8), k8 = (it % (kBK / 8)) * 8;
+        ring[u].hd[i].store(sH + m * kLD + k8);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t a = (&ring[u].w0.u.x)[j >> 1], b = (&ring[u].w1.u.x)[j >> 1];
+        if (kKind == kAB) {  // exactly one of the two descriptors was in range
+          a |= (&ring[u].b0.u.x)[j >> 1];
+          b |= (&ring[u].b1.u.x)[j >> 1];
         }
-      } else {
-        const uint16_t* Wa = static_cast<const uint16_t*>(p.W_a);
-        const uint16_t* Wb = static_cast<const uint16_t*>(p.W_b);
+        *reinterpret_cast<uint32_t*>(sWt + (n8 + j) * kLD + kp) =
+            __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
+      }
+      load(ring[u], kt + kRing);
+      __syncthreads();
+      if (kt < nkt) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = n + j;
-          e[j] = c < p.Hv ? Wa[(size_t)(k0 + k) * p.Hv + c]
-                          : (c < 2 * p.Hv ? Wb[(size_t)(k0 + k) * p.Hv + c - p.Hv] : (uint16_t)0);
+        for (int s = 0; s < kBK / 32; ++s) {
+          const Vec8<__bf16> a = Vec8<__bf16>::load(sH + (16 * w + lr) * kLD + 32 * s + 8 * lg);
+#pragma unroll
+          for (int nb = 0; nb < kBN / 16; ++nb)
+            acc[nb] = Mfma<__bf16>::mma(a, Vec8<__bf16>::load(sWt + (16 * nb + lr) * kLD + 32 * s + 8 * lg),
+                                        acc[nb]);
         }
       }
-      uint16_t* dst = reinterpret_cast<uint16_t*>(sWt);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dst[(n8 + j) * kLD + k] = e[j];
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-      const Vec8<__bf16> a = Vec8<__bf16>::load(sH + (16 * w + lr) * kLD + 32 * s + 8 * lg);
-#pragma unroll
-      for (int nb = 0; nb < kBN / 16; ++nb) {
-        const Vec8<__bf16> bfr = Vec8<__bf16>::load(sWt + (16 * nb + lr) * kLD + 32 * s + 8 * lg);
-        acc[nb] = Mfma<__bf16>::mma(a, bfr, acc[nb]);
-      }
-    }
-    __syncthreads();
   }
 
   // epilogue: lane holds Y[m0 + 16w + 4lg + r][n0 + 16nb + lr]
 #pragma unroll
   for (int nb = 0; nb < kBN / 16; ++nb) {
-    const int n = n0 + 16 * nb + lr;
-    if (n >= ncols) continue;
+    const int nn = n0 + 16 * nb + lr;
+    if (nn >= ncols) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + 16 * w + 4 * lg + r;
@@ -119,25 +195,38 @@ __global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams 
       const __bf16 y = f2bf(acc[nb][r]);
       if (seg == 0) {
         const int KW = p.K_win;
-        const __bf16* st = static_cast<const __bf16*>(p.conv_state_in) + ((size_t)m * conv_dim + n) * KW;
-        __bf16* so = static_cast<__bf16*>(p.conv_state_out) + ((size_t)m * conv_dim + n) * KW;
-        const float* cw = p.conv_weight + (size_t)n * KW;
+        const __bf16* st = static_cast<const __bf16*>(p.conv_state_in) + ((size_t)m * conv_dim + nn) * KW;
+        __bf16* so = static_cast<__bf16*>(p.conv_state_out) + ((size_t)m * conv_dim + nn) * KW;
+        const float* cw = p.conv_weight + (size_t)nn * KW;
         __bf16 win[8];
         for (int j = 0; j + 1 < KW; ++j) win[j] = st[j + 1];
         win[KW - 1] = y;
         float sum = 0.f;
         for (int j = 0; j < KW; ++j) sum += cw[j] * bf2f(win[j]);
         for (int j = 0; j < KW; ++j) so[j] = win[j];
-        static_cast<__bf16*>(p.ws_conv_out)[(size_t)m * conv_dim + n] = f2bf(sum * sigmoidf_(sum));
+        static_cast<__bf16*>(p.ws_conv_out)[(size_t)m * conv_dim + nn] = f2bf(sum * sigmoidf_(sum));
       } else if (seg == 1) {
-        static_cast<__bf16*>(p.ws_z)[(size_t)m * value_dim + n] = y;
-      } else if (n < p.Hv) {
-        p.ws_a[(size_t)m * p.Hv + n] = bf2f(y);
+        static_cast<__bf16*>(p.ws_z)[(size_t)m * value_dim + nn] = y;
+      } else if (nn < p.Hv) {
+        p.ws_a[(size_t)m * p.Hv + nn] = bf2f(y);
       } else {
-        p.ws_b[(size_t)m * p.Hv + n - p.Hv] = bf2f(y);
+        p.ws_b[(size_t)m * p.Hv + nn - p.Hv] = bf2f(y);
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams p) {
+  __shared__ __align__(16) __bf16 sH[kBM * kLD];
+  __shared__ __align__(16) __bf16 sWt[kBN * kLD];
+  const int conv_dim = 2 * p.Hk * p.Dk + p.Hv * p.Dv;
+  const int nt_main = (conv_dim + kBN - 1) / kBN + (p.Hv * p.Dv + kBN - 1) / kBN;
+  if ((int)blockIdx.x < nt_main)
+    block_proj_body<kSingle>(p, sH, sWt);
+  else if (p.Hv % 8 == 0)
+    block_proj_body<kAB>(p, sH, sWt);
+  else
+    block_proj_body<kABScalar>(p, sH, sWt);
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }

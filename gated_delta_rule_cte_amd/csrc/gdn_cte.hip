@@ -5,28 +5,29 @@
 // gam = inclusive cumsum of g_log inside the chunk, Gam = exp(gam)):
 //   A[t,i] = beta_t (k_t.k_i) exp(gam_t - gam_i)  for i < t        (strict lower)
 //   T      = (I + A)^-1                                            (unit lower)
+//   P[t,i] = scale (q_t.k_i) exp(gam_t - gam_i)   for i <= t
 //   X      = beta * (V - Gam * (K H))
-//   U      = T X                           (the per-token "new values" u_t)
-//   O      = scale (Gam * (Q H) + P U),  P[t,i] = (q_t.k_i) exp(gam_t - gam_i), i <= t
+//   U      = T X                                   (the per-token new values)
+//   O      = scale Gam * (Q H) + P U
 //   H'     = Gam_C H + (exp(gam_C - gam) * K)^T U
 // which is the token recurrence S_t = exp(g_t)(I - beta_t k_t k_t^T) S_{t-1}
 // + beta_t k_t v_t^T, o_t = scale S_t^T q_t rewritten exactly.  Every decay
 // factor is exp of a non-positive number, so nothing overflows.
 //
-// Every state column evolves independently, so one workgroup owns one
-// (batch, value head, DVT-column tile) and carries its [DK, DVT] slice of the
-// fp32 state in MFMA accumulators across all chunks.  The chunk-local products
-// (K K^T, Q K^T, T) are recomputed by each tile's workgroup.
-//
-// Per chunk (4 waves, LDS-staged, barriers between phases):
-//   0  coalesced loads of the K, Q, V tiles; wave 0 scans g_log
-//   1  K~^T = (exp(gam_C - gam) K)^T built in LDS; K K^T -> A, Q K^T -> P on
-//      MFMA (lower blocks only); K H -> X; Q H -> O accumulators
-//   2  T = (I + A)^-1: 16x16 diagonal blocks by forward substitution (one lane
-//      per column), off-diagonal blocks T_ij = -T_ii sum_m A_im T_mj level by
-//      level on fp32 MFMA
-//   3  U = T X (MFMA)
-//   4  O += P U -> out;  H = Gam_C H + K~^T U (MFMA into the state accumulators)
+// Two kernels:
+//  1. cte_local_kernel, one workgroup per (batch, value head, chunk), all
+//     chunks in parallel: K K^T and Q K^T on MFMA with the decays applied in
+//     the epilogue, then (I + A)^-1 by blocked forward substitution (16x16
+//     diagonal blocks one lane per column, off-diagonal blocks
+//     T_ij = -T_ii sum_m A_im T_mj level by level on fp32 MFMA); T and P go to
+//     the workspace with 16-byte stores.  Nothing here depends on the state.
+//  2. cte_state_kernel, one workgroup per (batch, value head, DVT state
+//     columns): the sequential pass over the chunks.  State columns evolve
+//     independently, so the workgroup carries its [DK, DVT] fp32 slice in
+//     MFMA accumulators.  Chunk data is prefetched into registers two chunks
+//     ahead and staged into LDS at the end of the previous chunk, leaving
+//     three barrier-separated phases per chunk on the critical path:
+//     K H -> X, Q H | U = T X | O = scale Gam Q H + P U, H' = Gam_C H + K~^T U.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -35,6 +36,20 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kC = 64;        // chunk length (one 16-row block per wave)
+constexpr int kNB = kC / 16;  // 16-token blocks per chunk
+
+#ifdef GDN_CTE_PROFILE
+constexpr int kProfSlots = 12;
+#define PROF_MARK(i)                                              \
+  if (tid == 0) {                                                 \
+    const unsigned long long now_ = __builtin_readcyclecounter(); \
+    prof_acc[i] += now_ - prof_last;                              \
+    prof_last = now_;                                             \
+  }
+#else
+#define PROF_MARK(i)
+#endif
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -55,50 +70,326 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, floa
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
-template <typename T, int DK, int DVT, int C>
-__global__ __launch_bounds__(kThreads) void cte_kernel(const CteParams p) {
+template <typename T>
+__device__ __forceinline__ void store2(T* p, float a, float b);
+template <>
+__device__ __forceinline__ void store2<float>(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+template <>
+__device__ __forceinline__ void store2<__bf16>(__bf16* p, float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, f2bf(a));
+  const uint32_t hi = __builtin_bit_cast(uint16_t, f2bf(b));
+  *reinterpret_cast<uint32_t*>(p) = lo | (hi << 16);
+}
+
+// K^T from token-major rows: element j of rows t0 and t0+1 -> one pair
+// {K[t0][c8+j], K[t0+1][c8+j]} at p (two consecutive tokens of one k row)
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, const Vec8<T>& r0, const Vec8<T>& r1, int j);
+template <>
+__device__ __forceinline__ void store_pair<float>(float* p, const Vec8<float>& r0, const Vec8<float>& r1, int j) {
+  *reinterpret_cast<float2*>(p) = make_float2(r0.get(j), r1.get(j));
+}
+template <>
+__device__ __forceinline__ void store_pair<__bf16>(__bf16* p, const Vec8<__bf16>& r0, const Vec8<__bf16>& r1,
+                                                   int j) {
+  const uint32_t a = (&r0.u.x)[j >> 1], b = (&r1.u.x)[j >> 1];
+  // v_perm_b32 byte select: low halves (j even) or high halves (j odd) of a, b
+  *reinterpret_cast<uint32_t*>(p) = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8), and each XCD has its own L2.  This remap gives XCD x the
+// contiguous logical ids [x n/8, (x+1) n/8), so workgroups that read the same
+// tiles (neighbouring logical ids) share one L2.  Identity when n % 8 != 0.
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int xcd_logical_id(int hw_id, int n) {
+  if (n % kXCDs != 0) return hw_id;
+  return (hw_id % kXCDs) * (n / kXCDs) + hw_id / kXCDs;
+}
+
+// T (bf16 or fp32) workspace of one (batch*value head, chunk): T then P, each [C][C]
+template <typename T>
+__device__ __forceinline__ T* ws_chunk(void* ws, int bh, int NC, int c) {
+  return static_cast<T*>(ws) + ((size_t)bh * NC + c) * 2 * kC * kC;
+}
+
+// ===========================================================================
+// kernel 1: chunk-local products and the triangular inverse
+// ===========================================================================
+// One workgroup per (batch * value head, chunk).  LDS: the K and Q tiles are
+// dead once the raw products sit in registers, so the fp32 A matrix reuses the
+// K tile's bytes and the staged P block the Q tile's.
+template <typename T, int DK>
+__global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) {
   using V8 = Vec8<T>;
   using MM = Mfma<T>;
-  constexpr int PAD = 16 / sizeof(T);   // 16 bytes of row padding against bank conflicts
-  constexpr int LDK = DK + PAD;         // pitch of [*, DK] tiles (K, Q, H^T)
-  constexpr int LDC = C + PAD;          // pitch of [*, C] tiles (K~^T, T, P, X^T, U^T)
-  constexpr int LDV = DVT + PAD;        // pitch of the V tile
-  constexpr int LDA = C + 1;            // pitch of the fp32 A and T tiles
-  constexpr int NB = C / 16;            // 16-token blocks per chunk
-  constexpr int NKB = DK / 16;
-  constexpr int NVB = DVT / 16;
-  constexpr int NHB = NKB * NVB;        // 16x16 blocks of the state tile
-  constexpr int HPW = NHB / kWaves;     // state blocks per wave
-  constexpr int NOT = NB * NVB;         // 16x16 output blocks per chunk
-  constexpr int OPW = (NOT + kWaves - 1) / kWaves;
-  static_assert(NHB % kWaves == 0, "state tile must split evenly over the waves");
-  static_assert(C % 32 == 0 && DK % 32 == 0 && DVT % 16 == 0, "tile shape");
+  constexpr int C = kC, NB = kNB;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LDK = DK + PAD;
+  constexpr int LDC = C + PAD;
+  constexpr int LDA = C + 4;                 // fp32 rows stay 16-byte aligned
+  constexpr int NIT = C * (DK / 8) / kThreads;
+  constexpr int kTileBytes = C * LDK * (int)sizeof(T);
+  constexpr int kABytes = C * LDA * 4;
+  constexpr int kPBytes = C * LDC * (int)sizeof(T);
+  constexpr int kBufBytes = (2 * kTileBytes > kABytes + kPBytes) ? 2 * kTileBytes : kABytes + kPBytes;
+  static_assert(NIT * kThreads == C * (DK / 8), "K/Q tile split");
 
-  __shared__ __align__(16) T sK[C * LDK];
-  __shared__ __align__(16) T sQ[C * LDK];
-  __shared__ __align__(16) T sKt[DK * LDC];
-  __shared__ __align__(16) T sHt[DVT * LDK];
-  __shared__ __align__(16) T sV[C * LDV];
-  __shared__ __align__(16) T sT[C * LDC];
-  __shared__ __align__(16) T sP[C * LDC];
-  __shared__ __align__(16) T sXt[DVT * LDC];
-  __shared__ __align__(16) T sUt[DVT * LDC];
-  __shared__ float sA[C * LDA];
-  __shared__ float sTf[C * LDA];
+  __shared__ __align__(16) char sbuf[kBufBytes];
+  __shared__ __align__(16) float sTf[C * LDA];
   __shared__ float sZ[kWaves][16 * 17];
   __shared__ float sGam[C];
   __shared__ float sBeta[C];
+  T* sK = reinterpret_cast<T*>(sbuf);
+  T* sQ = reinterpret_cast<T*>(sbuf + kTileBytes);
+  float* sA = reinterpret_cast<float*>(sbuf);           // after the raw products
+  T* sPs = reinterpret_cast<T*>(sbuf + kABytes);         // staged P, after the raw products
 
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int lane = tid & (kWave - 1);
-  const int lr = lane & 15;
-  const int lg = lane >> 4;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int S = p.S, Dk = p.Dk, Hk = p.Hk, Hv = p.Hv;
+  const int NC = (S + C - 1) / C;
+  // logical id = ((b * Hk + hk) * NC + c) * G + hh: the G value heads that
+  // share a key head's chunk are neighbours (and so share an XCD's L2)
+  const int G = Hv / Hk;
+  const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
+  const int hh = lid % G;
+  const int c = (lid / G) % NC;
+  const int bhk = lid / (G * NC);
+  const int b = bhk / Hk, hk = bhk - b * Hk;
+  const int h = hk * G + hh;
+  const int bh = b * Hv + h;
+  const int c0 = c * C, nvalid = min(C, S - c0);
+  const float scale = p.scale;
 
+  // K, Q chunk tiles (all loads issued before the first store); g, beta
+  {
+    const T* kg = static_cast<const T*>(p.k) + ((size_t)(b * Hk + hk) * S + c0) * Dk;
+    const T* qg = static_cast<const T*>(p.q) + ((size_t)(b * Hk + hk) * S + c0) * Dk;
+    V8 kr[NIT], qr[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int it = tid + kThreads * i, t = it / (DK / 8), c8 = (it % (DK / 8)) * 8;
+      const bool ok = t < nvalid && c8 < Dk;
+      kr[i] = ok ? V8::load(kg + (size_t)t * Dk + c8) : V8::zero();
+      qr[i] = ok ? V8::load(qg + (size_t)t * Dk + c8) : V8::zero();
+    }
+    float gl = 0.f, be = 0.f;
+    if (w == 0 && lane < nvalid) {
+      gl = p.g[(size_t)bh * S + c0 + lane];
+      be = p.beta[(size_t)bh * S + c0 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int it = tid + kThreads * i, t = it / (DK / 8), c8 = (it % (DK / 8)) * 8;
+      kr[i].store(sK + t * LDK + c8);
+      qr[i].store(sQ + t * LDK + c8);
+    }
+    if (w == 0) {
+      sGam[lane] = wave_inclusive_scan_dpp(gl);
+      sBeta[lane] = be;
+    }
+  }
+  __syncthreads();
+
+  // raw K K^T for row block w and Q K^T for row block NB-1-w (lower blocks)
+  const int rk = w, rq = NB - 1 - w;
+  f4 kk[NB], qk[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    kk[j] = f4{0.f, 0.f, 0.f, 0.f};
+    qk[j] = f4{0.f, 0.f, 0.f, 0.f};
+    if (j <= rk) {
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s)
+        kk[j] = MM::mma(V8::load(sK + (16 * rk + lr) * LDK + 32 * s + 8 * lg),
+                        V8::load(sK + (16 * j + lr) * LDK + 32 * s + 8 * lg), kk[j]);
+    }
+    if (j <= rq) {
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s)
+        qk[j] = MM::mma(V8::load(sQ + (16 * rq + lr) * LDK + 32 * s + 8 * lg),
+                        V8::load(sK + (16 * j + lr) * LDK + 32 * s + 8 * lg), qk[j]);
+    }
+  }
+  __syncthreads();  // K, Q tiles are dead from here on
+
+  // decays: A (fp32) into the K tile's bytes, P (compute type) into the Q tile's
+  {
+    float gt[4], bt[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      gt[r] = sGam[16 * rk + 4 * lg + r];
+      bt[r] = sBeta[16 * rk + 4 * lg + r];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j <= rk) {
+        const int i = 16 * j + lr;
+        const float gi = sGam[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * rk + 4 * lg + r;
+          sA[t * LDA + i] = (i < t) ? bt[r] * kk[j][r] * __expf(gt[r] - gi) : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gt[r] = sGam[16 * rq + 4 * lg + r];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j <= rq) {
+        const int i = 16 * j + lr;
+        const float gi = sGam[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * rq + 4 * lg + r;
+          sPs[t * LDC + i] = from_f32<T>((i <= t) ? scale * qk[j][r] * __expf(gt[r] - gi) : 0.f);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // diagonal 16x16 blocks of T: lane = (block, column), forward substitution
+  if (w == 0) {
+    const int blk = lane >> 4, j = lane & 15;
+    const float* Ab = sA + 16 * blk * LDA + 16 * blk;
+    float tc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float row[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(Ab + i * LDA + 4 * q);
+        row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
+      if (i > j) tc[i] = -acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
+  }
+  __syncthreads();
+
+  // off-diagonal blocks, one level (block distance d) at a time
+#pragma unroll
+  for (int d = 1; d < NB; ++d) {
+    const int bj = w, bi = w + d;
+    if (bi < NB) {
+      f4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int m = bj; m < bi; ++m) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * bi + lr) * LDA + 16 * m + 4 * s + lg],
+                                                   sTf[(16 * m + 4 * s + lg) * LDA + 16 * bj + lr], z, 0, 0, 0);
+      }
+      float* Zw = sZ[w];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Zw[(4 * lg + r) * 17 + lr] = z[r];
+      wave_lds_sync();
+      f4 tz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        tz = __builtin_amdgcn_mfma_f32_16x16x4f32(sTf[(16 * bi + lr) * LDA + 16 * bi + 4 * s + lg],
+                                                  Zw[(4 * s + lg) * 17 + lr], tz, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sTf[(16 * bi + 4 * lg + r) * LDA + 16 * bj + lr] = -tz[r];
+    }
+    __syncthreads();
+  }
+
+  // T (lower blocks, rounded to the compute type) and P -> workspace, 16-byte stores
+  T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
+  T* Pg = Tg + C * C;
+#pragma unroll
+  for (int i = 0; i < C * (C / 8) / kThreads; ++i) {
+    const int it = tid + kThreads * i, t = it / (C / 8), c8 = (it % (C / 8)) * 8;
+    if ((c8 >> 4) > (t >> 4)) continue;  // upper blocks are never read
+    const float* src = sTf + t * LDA + c8;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 bq = *reinterpret_cast<const float4*>(src + 4);
+    V8 v;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 f;
+      f[0] = f2bf(a.x); f[1] = f2bf(a.y); f[2] = f2bf(a.z); f[3] = f2bf(a.w);
+      f[4] = f2bf(bq.x); f[5] = f2bf(bq.y); f[6] = f2bf(bq.z); f[7] = f2bf(bq.w);
+      v.u = __builtin_bit_cast(uint4, f);
+    } else {
+      v.a = a;
+      v.b = bq;
+    }
+    v.store(Tg + t * C + c8);
+    V8::load(sPs + t * LDC + c8).store(Pg + t * C + c8);
+  }
+}
+
+// ===========================================================================
+// kernel 2: the sequential state pass
+// ===========================================================================
+// Per chunk c, three phases separated by workgroup barriers (wave w owns the
+// 16-token row block w of the chunk and the state blocks hb = w + 4j):
+//   B  store the outputs of chunk c-1; K H -> X = beta (V - Gam K H) -> LDS;
+//      Q H -> output accumulators
+//   C  U = T X -> LDS twice: as is (for P U) and scaled by d_t =
+//      exp(gam_C - gam_t) (for the state update, K~^T U = K^T (d U))
+//   D  O = scale Gam Q H + P U -> LDS (stored in the next B);
+//      H' = Gam_C H + K^T (d U) in the accumulators, bf16 copy -> LDS;
+//      then chunk c+1 is staged from the registers it was prefetched into
+//      during chunk c-1 (K, and K^T into the other half of a double buffer,
+//      V, g scan, beta into LDS; Q, T, P fragments stay in registers) and
+//      chunk c+2 is prefetched.
+// Every load and store goes through a buffer descriptor rebuilt per chunk
+// (scalar work) whose base is the chunk start and whose range ends at the
+// sequence end: per-thread offsets are loop invariant, and the hardware range
+// check zero-fills (or drops) the rows past a ragged end.
+template <typename T, int DK, int DVT>
+__global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) {
+  using V8 = Vec8<T>;
+  using MM = Mfma<T>;
+  constexpr int C = kC;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LDK = DK + PAD;
+  constexpr int LDC = C + PAD;
+  constexpr int LDV = DVT + PAD;
+  constexpr int NKB = DK / 16, NVB = DVT / 16;
+  constexpr int KG = DK / 32;                         // 32-column groups of K
+  constexpr int HPW = NKB * NVB / kWaves;             // state blocks per wave
+  constexpr int NKI = (C / 2) * (DK / 8) / kThreads;  // K token-pair items per thread
+  constexpr int NVT = C * (DVT / 8);                  // V / O items
+  constexpr int NV = (NVT + kThreads - 1) / kThreads;
+  constexpr int NQ = DK / 32;                         // Q fragments per lane
+  constexpr int KSTEPS = C / 32;
+  constexpr uint32_t ES = sizeof(T);
+  static_assert(NKB * NVB % kWaves == 0 && NKI * kThreads == (C / 2) * (DK / 8), "tile split");
+
+  __shared__ __align__(16) T sK[C * LDK];
+  __shared__ __align__(16) T sKt[2][DK * LDC];
+  __shared__ __align__(16) T sV[C * LDV];
+  __shared__ __align__(16) T sHt[DVT * LDK];
+  __shared__ __align__(16) T sXt[DVT * LDC];
+  __shared__ __align__(16) T sUt[DVT * LDC];
+  __shared__ __align__(16) T sUd[DVT * LDC];
+  __shared__ __align__(16) T sO[C * LDV];
+  __shared__ float sGam[C];
+  __shared__ float sBeta[C];
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+  const int lr = lane & 15, lg = lane >> 4;
   const int S = p.S, Dk = p.Dk, Dv = p.Dv, Hv = p.Hv;
+  const int NC = (S + C - 1) / C;
   const int ntiles = (Dv + DVT - 1) / DVT;
-  const int tile = blockIdx.x % ntiles;
-  const int bh = blockIdx.x / ntiles;
+  // logical id = (b * Hv + h) * ntiles + tile: the tiles of a head and the
+  // value heads of a key head are neighbours (and so share an XCD's L2)
+  const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
+  const int tile = lid % ntiles;
+  const int bh = lid / ntiles;
   const int b = bh / Hv, h = bh - b * Hv;
   const int hk = h / (Hv / p.Hk);
   const int col0 = tile * DVT;
@@ -112,272 +403,276 @@ __global__ __launch_bounds__(kThreads) void cte_kernel(const CteParams p) {
   T* og = static_cast<T*>(p.out) + (size_t)bh * S * Dv;
   float* stg = p.state + (size_t)bh * Dk * Dv;
 
-  // upper blocks of T and P are never written: zero them once
-  for (int i = tid; i < C * LDC; i += kThreads) {
-    sT[i] = from_f32<T>(0.f);
-    sP[i] = from_f32<T>(0.f);
-  }
-  for (int i = tid; i < C * LDA; i += kThreads) sTf[i] = 0.f;
-
-  // state tile -> accumulators (wave w owns blocks hb = w + 4j)
+  // state tile -> accumulators; wave w owns blocks hb = w + 4j (kb = hb / NVB, vb = hb % NVB)
   f4 hacc[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
-    const int c = col0 + 16 * vb + lr;
+    const int cc = col0 + 16 * vb + lr;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int kk = 16 * kb + 4 * lg + r;
-      hacc[j][r] = (p.has_initial_state && kk < Dk && c < Dv) ? stg[(size_t)kk * Dv + c] : 0.f;
+      hacc[j][r] = (p.has_initial_state && kk < Dk && cc < Dv) ? stg[(size_t)kk * Dv + cc] : 0.f;
     }
-    T* dst = sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg;
-    store4<T>(dst, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
+    store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
   }
 
-  f4 oacc[OPW];
+#ifdef GDN_CTE_PROFILE
+  unsigned long long prof_acc[kProfSlots] = {};
+  unsigned long long prof_last = __builtin_readcyclecounter();
+#endif
 
-  for (int c0 = 0; c0 < S; c0 += C) {
-    const int nvalid = min(C, S - c0);
+  // ---- loop-invariant per-thread offsets (bytes from the chunk start)
+  // K: item i = rows t0, t0+1 (t0 = 2 tp) at columns c8..c8+7; the 16 lanes
+  //    of a lane group take 16 consecutive token pairs, so the K^T stores of a
+  //    lane group are 16 consecutive dwords.
+  int kt0[NKI], kc8[NKI];
+  uint32_t vo_k[NKI];
+#pragma unroll
+  for (int i = 0; i < NKI; ++i) {
+    const int rest = w + kWaves * i;
+    kt0[i] = 2 * (lr + 16 * (rest / KG));
+    kc8[i] = 8 * lg + 32 * (rest % KG);
+    vo_k[i] = kc8[i] < Dk ? (uint32_t)(kt0[i] * Dk + kc8[i]) * ES : kOOB;
+  }
+  // T and P are only A operands of this wave's 16 rows: their fragments go
+  // straight into registers; upper 16x16 blocks read as zero
+  const int nks = (16 * (w + 1) + 31) / 32;           // k-steps touching lower blocks
+  uint32_t vo_t[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int k8 = 32 * s + 8 * lg;
+    vo_t[s] = (s < nks && (k8 >> 4) <= w) ? (uint32_t)((16 * w + lr) * C + k8) * ES : kOOB;
+  }
+  uint32_t vo_v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int it = tid + kThreads * i, t = it / (DVT / 8), c8 = (it % (DVT / 8)) * 8;
+    vo_v[i] = (it < NVT && col0 + c8 < Dv) ? (uint32_t)(t * Dv + col0 + c8) * ES : kOOB;
+  }
+  uint32_t vo_q[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const int k8 = 32 * s + 8 * lg;
+    vo_q[s] = k8 < Dk ? (uint32_t)((16 * w + lr) * Dk + k8) * ES : kOOB;
+  }
 
-    // ---------------------------------------------------------------- 0 loads
-    for (int it = tid; it < C * (DK / 8); it += kThreads) {
-      const int t = it / (DK / 8), c8 = (it % (DK / 8)) * 8;
-      const bool ok = t < nvalid && c8 < Dk;
-      const size_t off = (size_t)(c0 + t) * Dk + c8;
-      (ok ? V8::load(kg + off) : V8::zero()).store(sK + t * LDK + c8);
-      (ok ? V8::load(qg + off) : V8::zero()).store(sQ + t * LDK + c8);
+  // ---- prefetch registers (one chunk)
+  V8 pk0[NKI], pk1[NKI], ptf[KSTEPS], ppf[KSTEPS], pv[NV], pq[NQ];
+  float pg = 0.f, pb = 0.f;
+  auto prefetch = [&](int c) {
+    const int c0 = c * C;
+    const uint32_t rem = (uint32_t)(S - c0);
+    const auto rK = make_rsrc(kg + (size_t)c0 * Dk, rem * Dk * ES);
+    const auto rQ = make_rsrc(qg + (size_t)c0 * Dk, rem * Dk * ES);
+    const auto rV = make_rsrc(vg + (size_t)c0 * Dv, rem * Dv * ES);
+    const auto rW = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), 2 * C * C * ES);
+    const auto rG = make_rsrc(gg + c0, rem * 4);
+    const auto rB = make_rsrc(bg + c0, rem * 4);
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+      pk0[i] = V8::bload(rK, vo_k[i]);
+      pk1[i] = V8::bload(rK, vo_k[i] + (uint32_t)Dk * ES);
     }
-    for (int it = tid; it < C * (DVT / 8); it += kThreads) {
-      const int t = it / (DVT / 8), c8 = (it % (DVT / 8)) * 8;
-      const bool ok = t < nvalid && col0 + c8 < Dv;
-      (ok ? V8::load(vg + (size_t)(c0 + t) * Dv + col0 + c8) : V8::zero()).store(sV + t * LDV + c8);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      ptf[s] = V8::bload(rW, vo_t[s]);
+      ppf[s] = V8::bload(rW, vo_t[s] + (uint32_t)(C * C) * ES);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) pv[i] = V8::bload(rV, vo_v[i]);
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) pq[s] = V8::bload(rQ, vo_q[s]);
+    pg = buf_load_f32(rG, (uint32_t)lane * 4u);
+    pb = buf_load_f32(rB, (uint32_t)lane * 4u);
+  };
+
+  // ---- stage the prefetched chunk c into LDS (K, K^T[c & 1], V, g scan, beta)
+  //      and registers (Q, T, P fragments)
+  V8 qf[NQ], tf[KSTEPS], pf[KSTEPS];
+  auto stage = [&](int c) {
+#ifdef GDN_CTE_PROFILE
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): time the wait for the prefetch on its own
+    PROF_MARK(5)
+#endif
+    T* kt = sKt[c & 1];
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+      const int t0 = kt0[i], c8 = kc8[i];
+      pk0[i].store(sK + t0 * LDK + c8);
+      pk1[i].store(sK + (t0 + 1) * LDK + c8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) store_pair<T>(kt + (c8 + j) * LDC + t0, pk0[i], pk1[i], j);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int it = tid + kThreads * i, t = it / (DVT / 8), c8 = (it % (DVT / 8)) * 8;
+      if (it < NVT) pv[i].store(sV + t * LDV + c8);
+    }
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) qf[s] = pq[s];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      tf[s] = ptf[s];
+      pf[s] = ppf[s];
     }
     if (w == 0) {
-      const bool ok = lane < nvalid;
-      const float gl = ok ? gg[c0 + lane] : 0.f;
-      const float be = ok ? bg[c0 + lane] : 0.f;
-      const float gam = wave_inclusive_scan(gl, lane);
-      if (lane < C) {
-        sGam[lane] = gam;
-        sBeta[lane] = be;
-      }
+      sGam[lane] = wave_inclusive_scan_dpp(pg);
+      sBeta[lane] = pb;
     }
-    __syncthreads();
+  };
 
-    // ------------------------------------------------- 1 chunk-local products
+  // outputs of chunk c sit in sO from its phase D until the next phase B
+  auto flush_out = [&](int c) {
+    const int c0 = c * C;
+    const auto rO = make_rsrc(og + (size_t)c0 * Dv, (uint32_t)(S - c0) * Dv * ES);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int it = tid + kThreads * i, t = it / (DVT / 8), c8 = (it % (DVT / 8)) * 8;
+      if (it < NVT) V8::load(sO + t * LDV + c8).bstore(rO, vo_v[i]);
+    }
+  };
+
+  if (NC > 0) {
+    prefetch(0);
+    stage(0);
+    if (NC > 1) prefetch(1);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    PROF_MARK(0)
+    // ------------------------------------------------------------------- B
+    if (c > 0) flush_out(c - 1);
+    f4 oacc[NVB];
+    float GC, dt[4];
     {
+      float Gt[4], bt[4];
       const float gC = sGam[C - 1];
-      for (int it = tid; it < C * (DK / 8); it += kThreads) {
-        const int t = it % C, c8 = (it / C) * 8;
-        const V8 kv = V8::load(sK + t * LDK + c8);
-        const float d = __expf(gC - sGam[t]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sKt[(c8 + j) * LDC + t] = from_f32<T>(kv.get(j) * d);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lg + r;
+        const float gt = sGam[t];
+        Gt[r] = __expf(gt);
+        dt[r] = __expf(gC - gt);
+        bt[r] = sBeta[t];
       }
-    }
-    {
-      // K K^T (A, strict lower) and Q K^T (P, lower incl. diagonal), lower 16x16 blocks
-      constexpr int NT1 = NB * (NB + 1) / 2;
-      for (int task = w; task < 2 * NT1; task += kWaves) {
-        const bool isA = task < NT1;
-        int tt = isA ? task : task - NT1;
-        int bi = 0;
-        while (tt > bi) { tt -= bi + 1; ++bi; }
-        const int bj = tt;
-        const T* X = isA ? sK : sQ;
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+      GC = __expf(gC);
+      V8 kf[NQ];
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-          const V8 a = V8::load(X + (16 * bi + lr) * LDK + 32 * s + 8 * lg);
-          const V8 bb = V8::load(sK + (16 * bj + lr) * LDK + 32 * s + 8 * lg);
-          acc = MM::mma(a, bb, acc);
+      for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sK + (16 * w + lr) * LDK + 32 * s + 8 * lg);
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        f4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+          const V8 hb = V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg);
+          kh = MM::mma(kf[s], hb, kh);
+          qh = MM::mma(qf[s], hb, qh);
         }
-        const int ii = 16 * bj + lr;
-        const float gi = sGam[ii];
+        const int cc = 16 * vb + lr;
+        float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * bi + 4 * lg + r;
-          if (isA) {
-            sA[t * LDA + ii] = (ii < t) ? sBeta[t] * acc[r] * __expf(sGam[t] - gi) : 0.f;
-          } else {
-            sP[t * LDC + ii] = from_f32<T>((ii <= t) ? scale * acc[r] * __expf(sGam[t] - gi) : 0.f);
-          }
+          const int t = 16 * w + 4 * lg + r;
+          x[r] = bt[r] * (to_f32<T>(sV[t * LDV + cc]) - Gt[r] * kh[r]);
+          oacc[vb][r] = scale * Gt[r] * qh[r];
         }
-      }
-      // K H -> X (to LDS, transposed) and Q H -> O accumulators
-#pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-        const int ot = w + kWaves * j;
-        if (ot < NOT) {
-          const int rb = ot / NVB, vb = ot % NVB;
-          f4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DK / 32; ++s) {
-            const V8 hb = V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg);
-            kh = MM::mma(V8::load(sK + (16 * rb + lr) * LDK + 32 * s + 8 * lg), hb, kh);
-            qh = MM::mma(V8::load(sQ + (16 * rb + lr) * LDK + 32 * s + 8 * lg), hb, qh);
-          }
-          const int c = 16 * vb + lr;
-          float x[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * rb + 4 * lg + r;
-            const float G = __expf(sGam[t]);
-            x[r] = sBeta[t] * (to_f32<T>(sV[t * LDV + c]) - G * kh[r]);
-            oacc[j][r] = scale * G * qh[r];
-          }
-          store4<T>(sXt + c * LDC + 16 * rb + 4 * lg, x[0], x[1], x[2], x[3]);
-        }
+        store4<T>(sXt + cc * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
     __syncthreads();
+    PROF_MARK(1)
 
-    // ------------------------------------------------------- 2 T = (I + A)^-1
-    if (w == 0) {
-      const int blk = lane >> 4, j = lane & 15;
-      if (blk < NB) {
-        const float* Ab = sA + 16 * blk * LDA + 16 * blk;
-        float tc[16];
+    // ------------------------------------------------------------------- C
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 1; i < 16; ++i) {
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < i; ++m) acc += Ab[i * LDA + m] * tc[m];
-          if (i > j) tc[i] = -acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
-          sT[(16 * blk + i) * LDC + 16 * blk + j] = from_f32<T>(tc[i]);
-        }
-      }
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < nks) u = MM::mma(tf[s], V8::load(sXt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), u);
+      const int off = (16 * vb + lr) * LDC + 16 * w + 4 * lg;
+      store4<T>(sUt + off, u[0], u[1], u[2], u[3]);
+      store4<T>(sUd + off, dt[0] * u[0], dt[1] * u[1], dt[2] * u[2], dt[3] * u[3]);
     }
     __syncthreads();
-#pragma unroll
-    for (int d = 1; d < NB; ++d) {
-      const int bj = w, bi = w + d;
-      if (bi < NB) {
-        // Z = sum_{m=bj}^{bi-1} A_{bi,m} T_{m,bj}
-        f4 z = {0.f, 0.f, 0.f, 0.f};
-        for (int m = bj; m < bi; ++m) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float av = sA[(16 * bi + lr) * LDA + 16 * m + 4 * s + lg];
-            const float tv = sTf[(16 * m + 4 * s + lg) * LDA + 16 * bj + lr];
-            z = __builtin_amdgcn_mfma_f32_16x16x4f32(av, tv, z, 0, 0, 0);
-          }
-        }
-        float* Zw = sZ[w];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Zw[(4 * lg + r) * 17 + lr] = z[r];
-        wave_lds_sync();
-        // T_{bi,bj} = -T_{bi,bi} Z
-        f4 tz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float tv = sTf[(16 * bi + lr) * LDA + 16 * bi + 4 * s + lg];
-          const float zv = Zw[(4 * s + lg) * 17 + lr];
-          tz = __builtin_amdgcn_mfma_f32_16x16x4f32(tv, zv, tz, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * bi + 4 * lg + r;
-          sTf[t * LDA + 16 * bj + lr] = -tz[r];
-          sT[t * LDC + 16 * bj + lr] = from_f32<T>(-tz[r]);
-        }
-      }
-      __syncthreads();
-    }
+    PROF_MARK(2)
 
-    // ----------------------------------------------------------- 3 U = T X
+    // ------------------------------------------------------------------- D
 #pragma unroll
-    for (int j = 0; j < OPW; ++j) {
-      const int ot = w + kWaves * j;
-      if (ot < NOT) {
-        const int rb = ot / NVB, vb = ot % NVB;
-        f4 u = {0.f, 0.f, 0.f, 0.f};
-        const int nks = (16 * (rb + 1) + 31) / 32;
-        for (int s = 0; s < nks; ++s) {
-          const V8 a = V8::load(sT + (16 * rb + lr) * LDC + 32 * s + 8 * lg);
-          const V8 xb = V8::load(sXt + (16 * vb + lr) * LDC + 32 * s + 8 * lg);
-          u = MM::mma(a, xb, u);
-        }
-        store4<T>(sUt + (16 * vb + lr) * LDC + 16 * rb + 4 * lg, u[0], u[1], u[2], u[3]);
-      }
-    }
-    __syncthreads();
-
-    // --------------------------------------- 4 outputs and the state update
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 o = oacc[vb];
 #pragma unroll
-    for (int j = 0; j < OPW; ++j) {
-      const int ot = w + kWaves * j;
-      if (ot < NOT) {
-        const int rb = ot / NVB, vb = ot % NVB;
-        f4 o = oacc[j];
-        const int nks = (16 * (rb + 1) + 31) / 32;
-        for (int s = 0; s < nks; ++s) {
-          const V8 a = V8::load(sP + (16 * rb + lr) * LDC + 32 * s + 8 * lg);
-          const V8 ub = V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg);
-          o = MM::mma(a, ub, o);
-        }
-        const int c = col0 + 16 * vb + lr;
-        if (c < Dv) {
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < nks) o = MM::mma(pf[s], V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * rb + 4 * lg + r;
-            if (t < nvalid) og[(size_t)(c0 + t) * Dv + c] = from_f32<T>(o[r]);
-          }
-        }
-      }
+      for (int r = 0; r < 4; ++r) sO[(16 * w + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
     }
     {
-      const float GC = __expf(sGam[C - 1]);
+      const T* kt = sKt[c & 1];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
-        f4 hcur = hacc[j];
-        hcur[0] *= GC; hcur[1] *= GC; hcur[2] *= GC; hcur[3] *= GC;
+        f4 hc = hacc[j];
+        hc[0] *= GC; hc[1] *= GC; hc[2] *= GC; hc[3] *= GC;
 #pragma unroll
-        for (int s = 0; s < C / 32; ++s) {
-          const V8 a = V8::load(sKt + (16 * kb + lr) * LDC + 32 * s + 8 * lg);
-          const V8 ub = V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg);
-          hcur = MM::mma(a, ub, hcur);
-        }
-        hacc[j] = hcur;
-        store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hcur[0], hcur[1], hcur[2], hcur[3]);
+        for (int s = 0; s < KSTEPS; ++s)
+          hc = MM::mma(V8::load(kt + (16 * kb + lr) * LDC + 32 * s + 8 * lg),
+                       V8::load(sUd + (16 * vb + lr) * LDC + 32 * s + 8 * lg), hc);
+        hacc[j] = hc;
+        store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
       }
     }
+    PROF_MARK(3)
+    if (c + 1 < NC) {
+      stage(c + 1);
+      PROF_MARK(6)
+      if (c + 2 < NC) prefetch(c + 2);
+      PROF_MARK(7)
+    }
     __syncthreads();
+    PROF_MARK(4)
   }
+  if (NC > 0) flush_out(NC - 1);
 
+#ifdef GDN_CTE_PROFILE
+  if (tid == 0 && p.prof) {
+    for (int i = 0; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
+  }
+#endif
   // final state tile -> HBM (fp32)
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
-    const int c = col0 + 16 * vb + lr;
-    if (c < Dv) {
+    const int cc = col0 + 16 * vb + lr;
+    if (cc < Dv) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = 16 * kb + 4 * lg + r;
-        if (kk < Dk) stg[(size_t)kk * Dv + c] = hacc[j][r];
+        if (kk < Dk) stg[(size_t)kk * Dv + cc] = hacc[j][r];
       }
     }
   }
 }
 
-template <typename T, int DK, int DVT, int C>
-hipError_t launch_one(const CteParams& p, hipStream_t stream) {
-  const int ntiles = (p.Dv + DVT - 1) / DVT;
-  const long grid = (long)p.B * p.Hv * ntiles;
-  hipLaunchKernelGGL((cte_kernel<T, DK, DVT, C>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+template <typename T, int DK, int DVT>
+hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
+  const int NC = (p.S + kC - 1) / kC;
+  if (NC > 0) {
+    const long grid1 = (long)p.B * p.Hv * NC;
+    hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long grid2 = (long)p.B * p.Hv * ((p.Dv + DVT - 1) / DVT);
+  hipLaunchKernelGGL((cte_state_kernel<T, DK, DVT>), dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 // number of compute units on the target (MI355X)
 constexpr long kCUs = 256;
 
+// widest state tile that still gives every CU a workgroup
 int pick_dvt(const CteParams& p, int max_dvt) {
 #ifdef GDN_CTE_FORCE_DVT
   return GDN_CTE_FORCE_DVT;
@@ -385,15 +680,21 @@ int pick_dvt(const CteParams& p, int max_dvt) {
   const long heads = (long)p.B * p.Hv;
   int dvt = 16;
   for (int cand = max_dvt; cand >= 16; cand /= 2) {
-    const long tiles = (p.Dv + cand - 1) / cand;
-    if (heads * tiles >= kCUs || cand == 16) { dvt = cand; break; }
+    if (heads * ((p.Dv + cand - 1) / cand) >= kCUs || cand == 16) {
+      dvt = cand;
+      break;
+    }
   }
-  // never wider than the (16-rounded) value dimension
   while (dvt > 16 && dvt / 2 >= ((p.Dv + 15) / 16) * 16) dvt /= 2;
   return dvt;
 }
 
 }  // namespace
+
+size_t cte_workspace_bytes(int B, int Hv, int S, int dtype) {
+  const size_t NC = (size_t)((S + kC - 1) / kC);
+  return (size_t)B * Hv * NC * 2 * kC * kC * (dtype == 1 ? 2 : 4);
+}
 
 hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream) {
   if ((long)p.B * p.Hv == 0) return hipSuccess;
@@ -401,21 +702,21 @@ hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream) {
   if (dtype == 1) {
     const int dvt = pick_dvt(p, 64);
     if (dk64) {
-      if (dvt == 64) return launch_one<__bf16, 64, 64, 64>(p, stream);
-      if (dvt == 32) return launch_one<__bf16, 64, 32, 64>(p, stream);
-      return launch_one<__bf16, 64, 16, 64>(p, stream);
+      if (dvt == 64) return launch_pair<__bf16, 64, 64>(p, stream);
+      if (dvt == 32) return launch_pair<__bf16, 64, 32>(p, stream);
+      return launch_pair<__bf16, 64, 16>(p, stream);
     }
-    if (dvt == 64) return launch_one<__bf16, 128, 64, 64>(p, stream);
-    if (dvt == 32) return launch_one<__bf16, 128, 32, 64>(p, stream);
-    return launch_one<__bf16, 128, 16, 64>(p, stream);
+    if (dvt == 64) return launch_pair<__bf16, 128, 64>(p, stream);
+    if (dvt == 32) return launch_pair<__bf16, 128, 32>(p, stream);
+    return launch_pair<__bf16, 128, 16>(p, stream);
   }
-  const int dvt = pick_dvt(p, 32);
+  // fp32 tiles are twice the bytes: with DK = 128 only the 16-column state
+  // tile fits the 160 KB of LDS
   if (dk64) {
-    if (dvt == 32) return launch_one<float, 64, 32, 32>(p, stream);
-    return launch_one<float, 64, 16, 32>(p, stream);
+    if (pick_dvt(p, 32) == 32) return launch_pair<float, 64, 32>(p, stream);
+    return launch_pair<float, 64, 16>(p, stream);
   }
-  if (dvt == 32) return launch_one<float, 128, 32, 32>(p, stream);
-  return launch_one<float, 128, 16, 32>(p, stream);
+  return launch_pair<float, 128, 16>(p, stream);
 }
 
 }  // namespace gdn

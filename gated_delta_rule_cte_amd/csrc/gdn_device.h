@@ -31,6 +31,30 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return f2bf(x); }
 
 // ---------------------------------------------------------------------------
+// Raw buffer loads.  A load through a buffer descriptor whose offset lies at or
+// beyond the descriptor's byte range returns zeros, so masked loads need no
+// branch or select: invalid lanes pass kOOB.  Branch-free loads also let a
+// software-pipelined loop keep prefetched values in their destination
+// registers (a select on a loaded value would force a wait for the load).
+// ---------------------------------------------------------------------------
+constexpr int kBufferWord3 = 0x00020000;  // raw, untyped, stride 0 (gfx9 family)
+constexpr uint32_t kOOB = 0x80000000u;    // beyond every range used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
 // 8-element vectors: the per-lane operand slice of one 16x32 MFMA fragment,
 // and the unit of global <-> LDS copies (16 B of bf16, 32 B of fp32).
 // ---------------------------------------------------------------------------
@@ -45,6 +69,14 @@ template <> struct Vec8<__bf16> {
     return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
   }
   __device__ __forceinline__ bf16x8 frag() const { return __builtin_bit_cast(bf16x8, u); }
+  // 16 bytes at byte offset `off` of buffer `r` (zeros when out of range)
+  __device__ __forceinline__ static Vec8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Vec8 v; v.u = buf_load16(r, off); return v;
+  }
+  // store to byte offset `off` of buffer `r` (dropped when out of range)
+  __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
+    buf_store16(u, r, off);
+  }
 };
 template <> struct Vec8<float> {
   float4 a, b;
@@ -56,6 +88,18 @@ template <> struct Vec8<float> {
     reinterpret_cast<float4*>(p)[0] = a; reinterpret_cast<float4*>(p)[1] = b;
   }
   __device__ __forceinline__ float get(int j) const { return j < 4 ? (&a.x)[j] : (&b.x)[j - 4]; }
+  // 32 bytes at byte offset `off` of buffer `r` (zeros when out of range)
+  __device__ __forceinline__ static Vec8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Vec8 v;
+    v.a = __builtin_bit_cast(float4, buf_load16(r, off));
+    v.b = __builtin_bit_cast(float4, buf_load16(r, off + 16u));
+    return v;
+  }
+  // store to byte offset `off` of buffer `r` (dropped when out of range)
+  __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
+    buf_store16(__builtin_bit_cast(uint4, a), r, off);
+    buf_store16(__builtin_bit_cast(uint4, b), r, off + 16u);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -93,13 +137,33 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
   return x;
 }
-// inclusive prefix sum over the 64 lanes
+// inclusive prefix sum over the 64 lanes (ds_bpermute based; any lane count)
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const float y = __shfl_up(x, off, kWave);
     if (lane >= off) x += y;
   }
+  return x;
+}
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, true));
+}
+
+// inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS round trip): Hillis-Steele inside each 16-lane row,
+// then lane 15 of a row is added to the next row, lane 31 to rows 2 and 3.
+// Must be called by the whole wave.
+__device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += dpp_move<kRowShr | 1, 0xF>(x);
+  x += dpp_move<kRowShr | 2, 0xF>(x);
+  x += dpp_move<kRowShr | 4, 0xF>(x);
+  x += dpp_move<kRowShr | 8, 0xF>(x);
+  x += dpp_move<kRowBcast15, 0xA>(x);
+  x += dpp_move<kRowBcast31, 0xC>(x);
   return x;
 }
 

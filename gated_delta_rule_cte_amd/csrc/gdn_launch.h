@@ -45,7 +45,14 @@ struct CteParams {
   int B, Hk, Hv, S, Dk, Dv;
   int has_initial_state;
   float scale;
+  // scratch: per (batch * value head, chunk of 64 tokens) the inverse T and
+  // the decayed Q K^T block P, each [64][64] in the compute type
+  void* ws;
+  // per-workgroup phase cycle counts, written only by builds compiled with
+  // GDN_CTE_PROFILE (a development aid); NULL otherwise
+  unsigned long long* prof;
 };
+size_t cte_workspace_bytes(int B, int Hv, int S, int dtype);
 hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode layer

@@ -11,7 +11,8 @@
 //   wave 0 normalises q and k.
 //
 //   r = S^T k^ and p = S^T q^ are reduced over the 8 row groups through LDS in
-//   a fixed order (bitwise reproducible), then per column
+//   a fixed order (bitwise reproducible; one thread per column, so few
+//   registers are live next to the state), then per column
 //     u = beta (v - alpha r),  S' = alpha S + k^ u^T,  o = alpha p + (k^.q^) u
 //   which equals o = S'^T q^ without a second pass over the state.
 #include "gdn_device.h"
@@ -25,6 +26,10 @@ constexpr int kColGroups = 32;                       // float4 column groups, V 
 constexpr int kRowGroups = kThreads / kColGroups;    // 8
 constexpr int kRowsPerThread = 128 / kRowGroups;     // 16
 constexpr float kL2Eps = 1e-6f;
+// buffer descriptor word 3 for raw (untyped, stride 0) buffers on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
+// cache policy: non-temporal (the state is streamed exactly once each way)
+constexpr int kNonTemporal = 2;
 
 template <typename T>
 __device__ __forceinline__ float4 load4(const T* p);
@@ -40,11 +45,11 @@ __device__ __forceinline__ float4 load4<__bf16>(const __bf16* p) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void tkg_kernel(const TkgParams p) {
+__global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
   __shared__ float s_q[128];
   __shared__ float s_k[128];
-  __shared__ float4 s_red_r[kRowGroups][kColGroups];
-  __shared__ float4 s_red_p[kRowGroups][kColGroups];
+  __shared__ float4 s_red[2][kRowGroups][kColGroups];  // partial S^T k^, S^T q^
+  __shared__ float4 s_tot[2][kColGroups];              // their sums over row groups
   __shared__ float s_scal[3];  // alpha, beta, k^.q^
 
   const int bh = blockIdx.x;
@@ -56,17 +61,27 @@ __global__ __launch_bounds__(kThreads) void tkg_kernel(const TkgParams p) {
   const int bi = bh / p.Hv, h = bh - bi * p.Hv;
   const bool col_ok = 4 * cg < V;
 
-  const float* Sin = p.state_in + (size_t)bh * K * V;
-  float* Sout = p.state_out + (size_t)bh * K * V;
+  // The head's state through buffer descriptors: one 32-bit VGPR offset per
+  // thread plus a uniform SGPR offset per row group keeps the 16 row
+  // addresses out of the VGPR budget.  K % 8 == 0, so row rg + 8i exists for
+  // every thread exactly when i < K/8 (uniform); threads past the last column
+  // group use an offset beyond the descriptor's range (loads return zero,
+  // stores are dropped).
+  const uint32_t head_bytes = (uint32_t)(K * V * 4);
+  const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(p.state_in + (size_t)bh * K * V), (short)0, head_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+      p.state_out + (size_t)bh * K * V, (short)0, head_bytes, kBufferFlags);
+  const uint32_t voff = col_ok ? (uint32_t)((rg * V + 4 * cg) * 4) : 0x40000000u;
+  const uint32_t row_step = (uint32_t)(kRowGroups * V * 4);
+  const int nrow = K / kRowGroups;
 
   // 1. this thread's state slab -> registers
-  float4 s[kRowsPerThread];
+  f4 s[kRowsPerThread];
 #pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int r = rg + kRowGroups * i;
-    s[i] = (r < K && col_ok) ? *reinterpret_cast<const float4*>(Sin + (size_t)r * V + 4 * cg)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  for (int i = 0; i < kRowsPerThread; ++i)
+    s[i] = (i < nrow) ? __builtin_amdgcn_raw_buffer_load_b128(rin, voff, i * row_step, kNonTemporal)
+                      : f4{0.f, 0.f, 0.f, 0.f};
 
   // 2. prologue (wave 0): l2norm(q) / sqrt(K), l2norm(k), beta, g
   if (tid < kWave) {
@@ -104,16 +119,20 @@ __global__ __launch_bounds__(kThreads) void tkg_kernel(const TkgParams p) {
     pr.x += s[i].x * kr; pr.y += s[i].y * kr; pr.z += s[i].z * kr; pr.w += s[i].w * kr;
     pp.x += s[i].x * qr; pp.y += s[i].y * qr; pp.z += s[i].z * qr; pp.w += s[i].w * qr;
   }
-  s_red_r[rg][cg] = pr;
-  s_red_p[rg][cg] = pp;
+  s_red[0][rg][cg] = pr;
+  s_red[1][rg][cg] = pp;
   __syncthreads();
-  float4 R = s_red_r[0][cg], P = s_red_p[0][cg];
+  {
+    // thread t sums one of the 2 x 128 columns over the 8 row groups (fixed order)
+    const float* red = reinterpret_cast<const float*>(s_red);
+    const int which = tid / 128, col = tid % 128;
+    float acc = red[(which * kRowGroups + 0) * 128 + col];
 #pragma unroll
-  for (int g = 1; g < kRowGroups; ++g) {
-    const float4 a = s_red_r[g][cg], b = s_red_p[g][cg];
-    R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
-    P.x += b.x; P.y += b.y; P.z += b.z; P.w += b.w;
+    for (int g = 1; g < kRowGroups; ++g) acc += red[(which * kRowGroups + g) * 128 + col];
+    reinterpret_cast<float*>(s_tot)[which * 128 + col] = acc;
   }
+  __syncthreads();
+  const float4 R = s_tot[0][cg], P = s_tot[1][cg];
 
   // 4. u = beta (v - alpha r), o = alpha p + (k^.q^) u
   const float alpha = s_scal[0], beta = s_scal[1], kq = s_scal[2];
@@ -126,16 +145,13 @@ __global__ __launch_bounds__(kThreads) void tkg_kernel(const TkgParams p) {
   }
 
   // 5. S' = alpha S + k^ u^T, written once (streaming stores)
-  if (col_ok) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const int r = rg + kRowGroups * i;
-      if (r < K) {
-        const float kr = s_k[r];
-        const f4 o4 = {alpha * s[i].x + kr * u.x, alpha * s[i].y + kr * u.y,
-                       alpha * s[i].z + kr * u.z, alpha * s[i].w + kr * u.w};
-        __builtin_nontemporal_store(o4, reinterpret_cast<f4*>(Sout + (size_t)r * V + 4 * cg));
-      }
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    if (i < nrow) {
+      const float kr = s_k[rg + kRowGroups * i];
+      const f4 o4 = {alpha * s[i].x + kr * u.x, alpha * s[i].y + kr * u.y,
+                     alpha * s[i].z + kr * u.z, alpha * s[i].w + kr * u.w};
+      __builtin_amdgcn_raw_buffer_store_b128(o4, rout, voff, i * row_step, kNonTemporal);
     }
   }
 

@@ -80,11 +80,18 @@ enum { GDN_CTE_ALGO_DEFAULT = 0 };
  *                and the MFMA operand type.  Accumulation, the decay cumsum,
  *                the triangular solve and the state are fp32 either way.
  *   algorithm    GDN_CTE_ALGO_DEFAULT; anything else -> GDN_ERR_UNSUPPORTED.
- *   workspace    scratch of gdn_cte_workspace_size() bytes (may be NULL when
- *                that size is 0).
+ *   workspace    device scratch of gdn_cte_workspace_size() bytes, 256-byte
+ *                aligned, disjoint from every other argument (may be NULL when
+ *                that size is 0).  It holds, per value head and chunk of 64
+ *                tokens, the intra-chunk inverse (I + A)^-1 and the decayed
+ *                query-key block, 2 * 64 * 64 elements of `dtype`; its contents
+ *                are undefined after the call.  NULL or too small ->
+ *                GDN_ERR_WORKSPACE.
  * Constraints: 1 <= Dk, Dv <= 128 and multiples of 8; Hv % Hk == 0 (value head
  * h reads key/query head h / (Hv / Hk)); S >= 0 with no divisibility
- * requirement (a ragged last chunk is handled); B, Hk >= 1.
+ * requirement (a ragged last chunk is handled) and S * 256 * sizeof(dtype)
+ * below 2^31 (about 4M bf16 tokens per call; longer sequences are chained
+ * through recurrent_state); B, Hk >= 1.
  */
 int gdn_cte(const void* query, const void* key, const void* value,
             const float* g_log, const float* beta, float scale,
@@ -153,7 +160,8 @@ int gdn_tkg(const void* q, const void* k, const void* v, const float* b,
  * Stage boundaries are bf16: the projections and the conv output are rounded
  * to bf16; a and b are widened to fp32 for the gate.
  * Constraints: H % 128 == 0; num_v_heads % num_k_heads == 0; head dims
- * 8..128, multiples of 8; 1 <= K_win <= 8; B >= 1.
+ * 8..128, multiples of 8; 1 <= K_win <= 8; B >= 0; H * conv_dim * 2 and
+ * B * H * 2 below 2^31 bytes.
  */
 int gdn_block_tkg(const void* hidden, const void* W_in_qkv, const void* W_in_z,
                   const void* W_in_a, const void* W_in_b,

@@ -48,9 +48,12 @@ def cte_call(lib, **kw):
     args.update(kw)
     p = addrs(7)
     ptrs = kw.get("ptrs", p)
+    need = lib.gdn_cte_workspace_size(args["B"], args["Hk"], args["Hv"], args["S"], args["Dk"], args["Dv"],
+                                      args["dtype"])
+    ws = kw.get("ws", ctypes.c_void_p(A + 20 * STEP))
     return lib.gdn_cte(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], 0.125, ptrs[5], args["has_init"],
                        ptrs[6], args["B"], args["Hk"], args["Hv"], args["S"], args["Dk"], args["Dv"],
-                       args["dtype"], args["algorithm"], None, 0, None)
+                       args["dtype"], args["algorithm"], ws, kw.get("ws_bytes", need), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -83,6 +86,18 @@ def test_cte_rejects_null_misaligned_and_aliased(lib):
     bad = list(p)
     bad[5] = ctypes.c_void_p(p[3].value)            # state on top of g_log
     assert cte_call(lib, ptrs=bad) == -5
+
+
+def test_cte_workspace_checks(lib):
+    need = lib.gdn_cte_workspace_size(1, 2, 4, 128, 64, 64, gdn.GDN_BF16)
+    assert need == 4 * 2 * 2 * 64 * 64 * 2          # Hv * chunks * (T, P) * 64 * 64 * bf16
+    assert lib.gdn_cte_workspace_size(1, 2, 4, 0, 64, 64, gdn.GDN_BF16) == 0
+    assert lib.gdn_cte_workspace_size(1, 2, 4, 65, 64, 64, gdn.GDN_F32) == 4 * 2 * 2 * 64 * 64 * 4
+    assert cte_call(lib, ws=None) == -6
+    assert cte_call(lib, ws_bytes=need - 1) == -6
+    assert cte_call(lib, ws=ctypes.c_void_p(A + 20 * STEP + 16)) == -4
+    assert cte_call(lib, ws=ctypes.c_void_p(A + 2 * STEP)) == -5   # on top of value
+    assert cte_call(lib, S=0, ws=None) == -9                        # no workspace needed
 
 
 def test_cte_valid_call_without_gpu_reports_device(lib):
