@@ -9,9 +9,11 @@
 // bandwidth.  One workgroup owns 32 output columns of one weight matrix and
 // 64 batch rows and walks H in steps of 128 on bf16 MFMA (16x16x32), keeping
 // four K tiles of loads in flight in a register ring (branch-free buffer
-// loads).  The weight tile arrives N-contiguous and is transposed two rows at
-// a time (v_perm pairs) while it is written to LDS, so both MFMA operands are
-// read as contiguous 16-byte fragments.
+// loads).  The weight tile is written to LDS as it arrives (N-contiguous rows)
+// and its MFMA fragments, whose contraction index runs down those rows, are
+// read back with transposed LDS reads.  For the common hidden sizes the K loop
+// is unrolled completely, so every wait on the ring is for exactly the tile
+// about to be staged.
 //
 // Epilogue per output element (b, n), all results rounded to bf16:
 //   q|k|v column c:  window = [state[b,c,1:], y];  act = silu(sum_j w[c,j] window[j])
@@ -27,21 +29,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBM = 64;     // batch rows per workgroup (one 16-row block per wave)
-constexpr int kBN = 32;     // output columns per workgroup
+#ifndef GDN_BLOCK_BN
+#define GDN_BLOCK_BN 32
+#endif
+constexpr int kBN = GDN_BLOCK_BN;  // output columns per workgroup
 constexpr int kBK = 128;    // hidden-dimension step
 constexpr int kRing = 4;    // K tiles in flight per workgroup (register ring)
-constexpr int kLD = kBK + 8;
+constexpr int kLD = kBK + 8;   // hidden tile pitch (elements)
+constexpr int kLDW = kBN + 8;  // weight tile pitch: 16-byte rows, 2-way banked transposed reads
 
-// weight pair items per thread per K tile: (kBK/2 row pairs) x (kBN/8 column groups)
-constexpr int kWItems = (kBK / 2) * (kBN / 8) / kThreads;
+// weight items per thread per K tile: kBK rows x (kBN/8) column groups
+constexpr int kWItems = kBK * (kBN / 8) / kThreads;
 // hidden items per thread per K tile: kBM rows x (kBK/8) column groups
 constexpr int kHItems = kBM * (kBK / 8) / kThreads;
-static_assert(kWItems == 1 && kHItems * kThreads == kBM * (kBK / 8), "tile split");
+static_assert(kWItems >= 1 && kWItems * kThreads == kBK * (kBN / 8) &&
+              kHItems * kThreads == kBM * (kBK / 8), "tile split");
 
 struct Ring {
-  Vec8<__bf16> w0, w1;           // weight rows k, k+1 at 8 columns
-  Vec8<__bf16> b0, b1;           // the same from W_in_b (a|b tile only)
-  Vec8<__bf16> hd[kHItems];      // hidden tile slice
+  Vec8<__bf16> w[kWItems];   // weight row k at 8 columns
+  Vec8<__bf16> wb[kWItems];  // the same from W_in_b (a|b tile only)
+  Vec8<__bf16> hd[kHItems];  // hidden tile slice
 };
 
 // Tile kinds, each its own instantiation so that every buffer descriptor is
@@ -54,8 +61,9 @@ struct Ring {
 //   kABScalar the a|b tile, Hv % 8 != 0: element by element
 enum { kSingle = 0, kAB = 1, kABScalar = 2 };
 
-template <int kKind>
-__device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH, __bf16* sWt) {
+// NKT: number of K tiles (H / 128) when known at compile time, else 0
+template <int kKind, int NKT>
+__device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH, __bf16* sW) {
 
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid & (kWave - 1), lr = lane & 15, lg = lane >> 4;
@@ -64,7 +72,7 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
   const int nt_qkv = (conv_dim + kBN - 1) / kBN;
   const int nt_z = (value_dim + kBN - 1) / kBN;
   const int H = p.H, B = p.B;
-  const int nkt = H / kBK;
+  const int nkt = NKT > 0 ? NKT : H / kBK;
 
   // column tile -> (matrix, first column); the a|b tile reads W_in_a then W_in_b
   int tile = blockIdx.x, seg, ncols;
@@ -81,9 +89,14 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
   // Branch-free loads: each element's buffer offset is loop invariant except
   // for the K-tile step, and masked-off elements (columns past the matrix,
   // batch rows past B, K tiles past H) fall outside the descriptor range.
-  // Weight item: rows kp, kp+1 (kp = 2 * (tid / 4)), columns n8..n8+7.
-  const int kp = 2 * (tid / (kBN / 8)), n8 = 8 * (tid % (kBN / 8));
-  const int n = n0 + n8;
+  // Weight item i: row kp = (tid + 256 i) / (kBN/8), columns n8..n8+7.
+  int kp[kWItems], n8[kWItems];
+#pragma unroll
+  for (int i = 0; i < kWItems; ++i) {
+    const int it = tid + kThreads * i;
+    kp[i] = it / (kBN / 8);
+    n8[i] = 8 * (it % (kBN / 8));
+  }
   // uniform per workgroup: the matrix this tile reads (the a|b tile: W_in_a)
   const __bf16* Wbase = seg == 0 ? static_cast<const __bf16*>(p.W_qkv)
                       : seg == 1 ? static_cast<const __bf16*>(p.W_z)
@@ -92,13 +105,18 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wbase, (uint32_t)((size_t)H * wstride * 2));
   const uint32_t wrow = (uint32_t)wstride * 2u;
   const uint32_t wstep = (uint32_t)kBK * wrow;  // bytes per K tile
+  const __amdgpu_buffer_rsrc_t rWb = make_rsrc(p.W_b, (uint32_t)((size_t)H * p.Hv * 2));
   // per lane: kSingle / kAB read column n of W (kAB: of W_in_a when n < Hv),
   // kAB reads W_in_b's column n - Hv through rWb
-  const bool in_a = kKind == kSingle ? n < ncols : n < p.Hv;
-  const uint32_t wvo = (kKind != kABScalar && in_a) ? ((uint32_t)kp * wrow + (uint32_t)n * 2u) : kOOB;
-  const __amdgpu_buffer_rsrc_t rWb = make_rsrc(p.W_b, (uint32_t)((size_t)H * p.Hv * 2));
-  const uint32_t wvob =
-      (kKind == kAB && n >= p.Hv && n < ncols) ? ((uint32_t)kp * wrow + (uint32_t)(n - p.Hv) * 2u) : kOOB;
+  uint32_t wvo[kWItems], wvob[kWItems];
+#pragma unroll
+  for (int i = 0; i < kWItems; ++i) {
+    const int n = n0 + n8[i];
+    const bool in_a = kKind == kSingle ? n < ncols : n < p.Hv;
+    wvo[i] = (kKind != kABScalar && in_a) ? ((uint32_t)kp[i] * wrow + (uint32_t)n * 2u) : kOOB;
+    wvob[i] = (kKind == kAB && n >= p.Hv && n < ncols) ? ((uint32_t)kp[i] * wrow + (uint32_t)(n - p.Hv) * 2u)
+                                                       : kOOB;
+  }
 
   const __amdgpu_buffer_rsrc_t rH = make_rsrc(p.hidden, (uint32_t)((size_t)B * H * 2));
   uint32_t hvo[kHItems];
@@ -110,29 +128,27 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
 
   auto load = [&](Ring& rg, int kt) {
     // K tiles past the end read zero (their offsets exceed the range)
-    const uint32_t wo = (kt < nkt && wvo != kOOB) ? wvo + (uint32_t)kt * wstep : kOOB;
-    rg.w0 = Vec8<__bf16>::bload(rW, wo);
-    rg.w1 = Vec8<__bf16>::bload(rW, wo == kOOB ? kOOB : wo + wrow);
-    if (kKind == kAB) {
-      const uint32_t wob = (kt < nkt && wvob != kOOB) ? wvob + (uint32_t)kt * wstep : kOOB;
-      rg.b0 = Vec8<__bf16>::bload(rWb, wob);
-      rg.b1 = Vec8<__bf16>::bload(rWb, wob == kOOB ? kOOB : wob + wrow);
-    }
-    if (kKind == kABScalar && kt < nkt) {
-      const uint16_t* Wa = static_cast<const uint16_t*>(p.W_a);
-      const uint16_t* Wb = static_cast<const uint16_t*>(p.W_b);
-      uint16_t e0[8], e1[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int cc = n + j;
-        const size_t r0 = (size_t)(kt * kBK + kp) * p.Hv, r1 = r0 + p.Hv;
-        e0[j] = cc < p.Hv ? Wa[r0 + cc] : (cc < 2 * p.Hv ? Wb[r0 + cc - p.Hv] : (uint16_t)0);
-        e1[j] = cc < p.Hv ? Wa[r1 + cc] : (cc < 2 * p.Hv ? Wb[r1 + cc - p.Hv] : (uint16_t)0);
+    for (int i = 0; i < kWItems; ++i) {
+      const uint32_t wo = (kt < nkt && wvo[i] != kOOB) ? wvo[i] + (uint32_t)kt * wstep : kOOB;
+      rg.w[i] = Vec8<__bf16>::bload(rW, wo);
+      if (kKind == kAB) {
+        const uint32_t wob = (kt < nkt && wvob[i] != kOOB) ? wvob[i] + (uint32_t)kt * wstep : kOOB;
+        rg.wb[i] = Vec8<__bf16>::bload(rWb, wob);
       }
-      rg.w0.u = make_uint4(e0[0] | (uint32_t)e0[1] << 16, e0[2] | (uint32_t)e0[3] << 16,
-                           e0[4] | (uint32_t)e0[5] << 16, e0[6] | (uint32_t)e0[7] << 16);
-      rg.w1.u = make_uint4(e1[0] | (uint32_t)e1[1] << 16, e1[2] | (uint32_t)e1[3] << 16,
-                           e1[4] | (uint32_t)e1[5] << 16, e1[6] | (uint32_t)e1[7] << 16);
+      if (kKind == kABScalar && kt < nkt) {
+        const uint16_t* Wa = static_cast<const uint16_t*>(p.W_a);
+        const uint16_t* Wb = static_cast<const uint16_t*>(p.W_b);
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int cc = n0 + n8[i] + j;
+          const size_t r = (size_t)(kt * kBK + kp[i]) * p.Hv;
+          e[j] = cc < p.Hv ? Wa[r + cc] : (cc < 2 * p.Hv ? Wb[r + cc - p.Hv] : (uint16_t)0);
+        }
+        rg.w[i].u = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                               e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kHItems; ++i)
@@ -147,25 +163,26 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
 #pragma unroll
   for (int u = 0; u < kRing; ++u) load(ring[u], u);
 
-  for (int kt0 = 0; kt0 < nkt; kt0 += kRing) {
+  auto ring_pass = [&](int kt0) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int kt = kt0 + u;
-      // stage tile kt: hidden rows as is, weight rows transposed in pairs
+      // stage tile kt: hidden and weight rows as they arrived
 #pragma unroll
       for (int i = 0; i < kHItems; ++i) {
         const int it = tid + kThreads * i, m = it / (kBK / 8), k8 = (it % (kBK / 8)) * 8;
         ring[u].hd[i].store(sH + m * kLD + k8);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t a = (&ring[u].w0.u.x)[j >> 1], b = (&ring[u].w1.u.x)[j >> 1];
+      for (int i = 0; i < kWItems; ++i) {
+        Vec8<__bf16> v = ring[u].w[i];
         if (kKind == kAB) {  // exactly one of the two descriptors was in range
-          a |= (&ring[u].b0.u.x)[j >> 1];
-          b |= (&ring[u].b1.u.x)[j >> 1];
+          v.u.x |= ring[u].wb[i].u.x;
+          v.u.y |= ring[u].wb[i].u.y;
+          v.u.z |= ring[u].wb[i].u.z;
+          v.u.w |= ring[u].wb[i].u.w;
         }
-        *reinterpret_cast<uint32_t*>(sWt + (n8 + j) * kLD + kp) =
-            __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
+        v.store(sW + kp[i] * kLDW + n8[i]);
       }
       load(ring[u], kt + kRing);
       __syncthreads();
@@ -175,12 +192,17 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
           const Vec8<__bf16> a = Vec8<__bf16>::load(sH + (16 * w + lr) * kLD + 32 * s + 8 * lg);
 #pragma unroll
           for (int nb = 0; nb < kBN / 16; ++nb)
-            acc[nb] = Mfma<__bf16>::mma(a, Vec8<__bf16>::load(sWt + (16 * nb + lr) * kLD + 32 * s + 8 * lg),
-                                        acc[nb]);
+            acc[nb] = Mfma<__bf16>::mma(a, lds_tr_frag(sW, kLDW, 32 * s, 16 * nb, lane), acc[nb]);
         }
       }
       __syncthreads();
     }
+  };
+  if constexpr (NKT > 0) {
+#pragma unroll
+    for (int kt0 = 0; kt0 < NKT; kt0 += kRing) ring_pass(kt0);
+  } else {
+    for (int kt0 = 0; kt0 < nkt; kt0 += kRing) ring_pass(kt0);
   }
 
   // epilogue: lane holds Y[m0 + 16w + 4lg + r][n0 + 16nb + lr]
@@ -216,17 +238,18 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
   }
 }
 
+template <int NKT>
 __global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams p) {
   __shared__ __align__(16) __bf16 sH[kBM * kLD];
-  __shared__ __align__(16) __bf16 sWt[kBN * kLD];
+  __shared__ __align__(16) __bf16 sW[kBK * kLDW];
   const int conv_dim = 2 * p.Hk * p.Dk + p.Hv * p.Dv;
   const int nt_main = (conv_dim + kBN - 1) / kBN + (p.Hv * p.Dv + kBN - 1) / kBN;
   if ((int)blockIdx.x < nt_main)
-    block_proj_body<kSingle>(p, sH, sWt);
+    block_proj_body<kSingle, NKT>(p, sH, sW);
   else if (p.Hv % 8 == 0)
-    block_proj_body<kAB>(p, sH, sWt);
+    block_proj_body<kAB, NKT>(p, sH, sW);
   else
-    block_proj_body<kABScalar>(p, sH, sWt);
+    block_proj_body<kABScalar, NKT>(p, sH, sW);
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -249,7 +272,13 @@ hipError_t launch_block_proj(const BlockParams& p, hipStream_t stream) {
   const int conv_dim = 2 * key_dim + value_dim;
   const int tiles = (conv_dim + kBN - 1) / kBN + (value_dim + kBN - 1) / kBN + (2 * p.Hv + kBN - 1) / kBN;
   const dim3 grid(tiles, (p.B + kBM - 1) / kBM);
-  hipLaunchKernelGGL(block_proj_kernel, grid, dim3(kThreads), 0, stream, p);
+  // hidden sizes 1024, 2048, 4096 get a fully unrolled K loop
+  switch (p.H / kBK) {
+    case 8: hipLaunchKernelGGL(block_proj_kernel<8>, grid, dim3(kThreads), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL(block_proj_kernel<16>, grid, dim3(kThreads), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(block_proj_kernel<32>, grid, dim3(kThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL(block_proj_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
+  }
   return hipGetLastError();
 }
 

@@ -83,22 +83,6 @@ __device__ __forceinline__ void store2<__bf16>(__bf16* p, float a, float b) {
   *reinterpret_cast<uint32_t*>(p) = lo | (hi << 16);
 }
 
-// K^T from token-major rows: element j of rows t0 and t0+1 -> one pair
-// {K[t0][c8+j], K[t0+1][c8+j]} at p (two consecutive tokens of one k row)
-template <typename T>
-__device__ __forceinline__ void store_pair(T* p, const Vec8<T>& r0, const Vec8<T>& r1, int j);
-template <>
-__device__ __forceinline__ void store_pair<float>(float* p, const Vec8<float>& r0, const Vec8<float>& r1, int j) {
-  *reinterpret_cast<float2*>(p) = make_float2(r0.get(j), r1.get(j));
-}
-template <>
-__device__ __forceinline__ void store_pair<__bf16>(__bf16* p, const Vec8<__bf16>& r0, const Vec8<__bf16>& r1,
-                                                   int j) {
-  const uint32_t a = (&r0.u.x)[j >> 1], b = (&r1.u.x)[j >> 1];
-  // v_perm_b32 byte select: low halves (j even) or high halves (j odd) of a, b
-  *reinterpret_cast<uint32_t*>(p) = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
 // XCD i % 8), and each XCD has its own L2.  This remap gives XCD x the
 // contiguous logical ids [x n/8, (x+1) n/8), so workgroups that read the same
@@ -342,9 +326,10 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
 //   D  O = scale Gam Q H + P U -> LDS (stored in the next B);
 //      H' = Gam_C H + K^T (d U) in the accumulators, bf16 copy -> LDS;
 //      then chunk c+1 is staged from the registers it was prefetched into
-//      during chunk c-1 (K, and K^T into the other half of a double buffer,
-//      V, g scan, beta into LDS; Q, T, P fragments stay in registers) and
-//      chunk c+2 is prefetched.
+//      during chunk c-1 (K into the other half of a double buffer, V, g scan,
+//      beta into LDS; Q, T, P fragments stay in registers) and chunk c+2 is
+//      prefetched.  The K^T operand of the state update is read from the
+//      token-major K tile with transposed LDS reads.
 // Every load and store goes through a buffer descriptor rebuilt per chunk
 // (scalar work) whose base is the chunk start and whose range ends at the
 // sequence end: per-thread offsets are loop invariant, and the hardware range
@@ -369,8 +354,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
   constexpr uint32_t ES = sizeof(T);
   static_assert(NKB * NVB % kWaves == 0 && NKI * kThreads == (C / 2) * (DK / 8), "tile split");
 
-  __shared__ __align__(16) T sK[C * LDK];
-  __shared__ __align__(16) T sKt[2][DK * LDC];
+  __shared__ __align__(16) T sKb[2][C * LDK];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
   __shared__ __align__(16) T sXt[DVT * LDC];
@@ -423,9 +407,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
 #endif
 
   // ---- loop-invariant per-thread offsets (bytes from the chunk start)
-  // K: item i = rows t0, t0+1 (t0 = 2 tp) at columns c8..c8+7; the 16 lanes
-  //    of a lane group take 16 consecutive token pairs, so the K^T stores of a
-  //    lane group are 16 consecutive dwords.
+  // K: item i = rows t0, t0+1 (t0 = 2 tp) at columns c8..c8+7
   int kt0[NKI], kc8[NKI];
   uint32_t vo_k[NKI];
 #pragma unroll
@@ -487,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
     pb = buf_load_f32(rB, (uint32_t)lane * 4u);
   };
 
-  // ---- stage the prefetched chunk c into LDS (K, K^T[c & 1], V, g scan, beta)
+  // ---- stage the prefetched chunk c into LDS (K[c & 1], V, g scan, beta)
   //      and registers (Q, T, P fragments)
   V8 qf[NQ], tf[KSTEPS], pf[KSTEPS];
   auto stage = [&](int c) {
@@ -495,14 +477,12 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): time the wait for the prefetch on its own
     PROF_MARK(5)
 #endif
-    T* kt = sKt[c & 1];
+    T* sK = sKb[c & 1];
 #pragma unroll
     for (int i = 0; i < NKI; ++i) {
       const int t0 = kt0[i], c8 = kc8[i];
       pk0[i].store(sK + t0 * LDK + c8);
       pk1[i].store(sK + (t0 + 1) * LDK + c8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_pair<T>(kt + (c8 + j) * LDC + t0, pk0[i], pk1[i], j);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -558,6 +538,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
         bt[r] = sBeta[t];
       }
       GC = __expf(gC);
+      const T* sK = sKb[c & 1];
       V8 kf[NQ];
 #pragma unroll
       for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sK + (16 * w + lr) * LDK + 32 * s + 8 * lg);
@@ -609,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
       for (int r = 0; r < 4; ++r) sO[(16 * w + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
     }
     {
-      const T* kt = sKt[c & 1];
+      const T* sK = sKb[c & 1];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
@@ -617,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
         hc[0] *= GC; hc[1] *= GC; hc[2] *= GC; hc[3] *= GC;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
-          hc = MM::mma(V8::load(kt + (16 * kb + lr) * LDC + 32 * s + 8 * lg),
+          hc = MM::mma(lds_tr_frag(sK, LDK, 32 * s, 16 * kb, lane),
                        V8::load(sUd + (16 * vb + lr) * LDC + 32 * s + 8 * lg), hc);
         hacc[j] = hc;
         store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
@@ -655,6 +636,354 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
   }
 }
 
+// ===========================================================================
+// kernel 2, bf16: the same sequential pass with four data-mover waves
+// ===========================================================================
+// Eight waves per workgroup.  Waves 0-3 compute exactly as above (wave w owns
+// row block w of the chunk and the state blocks w + 4j) but issue no global
+// memory instruction inside the chunk loop; waves 4-7 only move data.  The
+// movers hold the next chunk's operands in their registers and write each
+// into LDS as soon as the compute phase that read the previous copy has passed
+// its barrier, then load the same operand of the chunk after that, so every
+// load has a whole chunk of time to arrive and the memory pipeline's issue
+// stalls fall on the movers:
+//   segment 1  compute: B          movers: P(c), K(c+1) -> LDS (K double
+//                                  buffered), outputs of c-1 -> HBM,
+//                                  load P(c+1), K(c+2)
+//   barrier
+//   segment 2  compute: C          movers: Q, V, g scan, beta of c+1 -> LDS,
+//                                  load those of c+2
+//   barrier
+//   segment 3  compute: D          movers: T(c+1) -> LDS, load T(c+2)
+//   barrier
+// Only the lower 16x16 blocks of T and P are moved; their upper blocks are
+// zeroed once and never written again.
+constexpr int kWsThreads = 512;
+constexpr int kMovers = kWsThreads - kThreads;  // mover threads
+constexpr int kTriItems = (kNB * (kNB + 1) / 2) * 16 * 2;  // 16-byte items in the lower blocks of a C x C tile
+
+template <int DK, int DVT>
+__global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParams p) {
+  using T = __bf16;
+  using V8 = Vec8<T>;
+  using MM = Mfma<T>;
+  constexpr int C = kC;
+  constexpr int PAD = 8;
+  constexpr int LDK = DK + PAD;
+  constexpr int LDC = C + PAD;
+  constexpr int LDV = DVT + PAD;
+  constexpr int NKB = DK / 16, NVB = DVT / 16;
+  constexpr int HPW = NKB * NVB / kWaves;                // state blocks per compute wave
+  constexpr int NQ = DK / 32;                            // Q / K fragments per lane
+  constexpr int KSTEPS = C / 32;
+  constexpr int NKQ = C * (DK / 8) / kMovers;            // K or Q items per mover thread
+  constexpr int NTP = (kTriItems + kMovers - 1) / kMovers;
+  constexpr int NVT = C * (DVT / 8);                     // V / O items
+  constexpr int NVI = (NVT + kMovers - 1) / kMovers;
+  constexpr uint32_t ES = 2;
+  static_assert(NKB * NVB % kWaves == 0 && NKQ * kMovers == C * (DK / 8), "tile split");
+  static_assert(NTP == 2 && kTriItems - kMovers <= kWave, "second T/P item belongs to mover wave 0 only");
+
+  __shared__ __align__(16) T sK[2][C * LDK];
+  __shared__ __align__(16) T sQ[C * LDK];
+  __shared__ __align__(16) T sT[C * LDC];
+  __shared__ __align__(16) T sP[C * LDC];
+  __shared__ __align__(16) T sV[C * LDV];
+  __shared__ __align__(16) T sHt[DVT * LDK];
+  __shared__ __align__(16) T sXt[DVT * LDC];
+  __shared__ __align__(16) T sUt[DVT * LDC];
+  __shared__ __align__(16) T sUd[DVT * LDC];
+  __shared__ __align__(16) T sO[C * LDV];
+  __shared__ float sGam[C];
+  __shared__ float sBeta[C];
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+  const int lr = lane & 15, lg = lane >> 4;
+  const bool mover = w >= kWaves;
+  const int mt = tid - kThreads;  // mover thread index (movers only)
+  const int S = p.S, Dk = p.Dk, Dv = p.Dv, Hv = p.Hv;
+  const int NC = (S + C - 1) / C;
+  const int ntiles = (Dv + DVT - 1) / DVT;
+  const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
+  const int tile = lid % ntiles;
+  const int bh = lid / ntiles;
+  const int b = bh / Hv, h = bh - b * Hv;
+  const int hk = h / (Hv / p.Hk);
+  const int col0 = tile * DVT;
+  const float scale = p.scale;
+
+  const T* qg = static_cast<const T*>(p.q) + (size_t)(b * p.Hk + hk) * S * Dk;
+  const T* kg = static_cast<const T*>(p.k) + (size_t)(b * p.Hk + hk) * S * Dk;
+  const T* vg = static_cast<const T*>(p.v) + (size_t)bh * S * Dv;
+  const float* gg = p.g + (size_t)bh * S;
+  const float* bg = p.beta + (size_t)bh * S;
+  T* og = static_cast<T*>(p.out) + (size_t)bh * S * Dv;
+  float* stg = p.state + (size_t)bh * Dk * Dv;
+
+  // upper blocks of T and P read as zero for good
+  for (int i = tid; i < C * LDC / 2; i += kWsThreads) {
+    reinterpret_cast<uint32_t*>(sT)[i] = 0u;
+    reinterpret_cast<uint32_t*>(sP)[i] = 0u;
+  }
+
+  f4 hacc[HPW];
+  if (!mover) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
+      const int cc = col0 + 16 * vb + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 16 * kb + 4 * lg + r;
+        hacc[j][r] = (p.has_initial_state && kk < Dk && cc < Dv) ? stg[(size_t)kk * Dv + cc] : 0.f;
+      }
+      store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
+    }
+  }
+
+#ifdef GDN_CTE_PROFILE
+  unsigned long long prof_acc[kProfSlots] = {};
+  unsigned long long prof_last = __builtin_readcyclecounter();
+#endif
+
+  // ---- mover state: loop-invariant offsets (bytes from the chunk start) and
+  //      LDS element offsets of every item, and the in-flight registers
+  uint32_t vo_kq[NKQ], vo_tp[NTP], vo_v[NVI];
+  int lo_kq[NKQ], lo_tp[NTP], lo_v[NVI];
+#pragma unroll
+  for (int i = 0; i < NKQ; ++i) {
+    const int it = mt + kMovers * i, t = it / (DK / 8), c8 = 8 * (it % (DK / 8));
+    vo_kq[i] = c8 < Dk ? (uint32_t)(t * Dk + c8) * ES : kOOB;
+    lo_kq[i] = t * LDK + c8;
+  }
+#pragma unroll
+  for (int i = 0; i < NTP; ++i) {
+    const int it = mt + kMovers * i;
+    const int bi = it / 32;                                  // lower block, row-major order
+    const int rb = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
+    const int cb = bi - rb * (rb + 1) / 2;
+    const int row = 16 * rb + (it % 32) / 2, col = 16 * cb + 8 * (it % 2);
+    vo_tp[i] = it < kTriItems ? (uint32_t)(row * C + col) * ES : kOOB;
+    lo_tp[i] = row * LDC + col;
+  }
+#pragma unroll
+  for (int i = 0; i < NVI; ++i) {
+    const int it = mt + kMovers * i, t = it / (DVT / 8), c8 = 8 * (it % (DVT / 8));
+    vo_v[i] = (it < NVT && col0 + c8 < Dv) ? (uint32_t)(t * Dv + col0 + c8) * ES : kOOB;
+    lo_v[i] = t * LDV + c8;
+  }
+  V8 rK[NKQ], rQ[NKQ], rT[NTP], rP[NTP], rV[NVI];
+  float rg = 0.f, rb_ = 0.f;
+
+  // descriptors of chunk c (range 0 past the last chunk: the loads read zero)
+  auto rem_bytes = [&](int c, int row_elems) -> uint32_t {
+    const int r = S - c * C;
+    return r > 0 ? (uint32_t)r * (uint32_t)row_elems * ES : 0u;
+  };
+  auto ld_k = [&](int c) {
+    const auto r = make_rsrc(kg + (size_t)c * C * Dk, rem_bytes(c, Dk));
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) rK[i] = V8::bload(r, vo_kq[i]);
+  };
+  auto ld_p = [&](int c) {
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < NC ? (uint32_t)(C * C) * ES : 0u);
+#pragma unroll
+    for (int i = 0; i < NTP; ++i) rP[i] = V8::bload(r, vo_tp[i]);
+  };
+  auto ld_t = [&](int c) {
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < NC ? (uint32_t)(C * C) * ES : 0u);
+#pragma unroll
+    for (int i = 0; i < NTP; ++i) rT[i] = V8::bload(r, vo_tp[i]);
+  };
+  auto ld_qvg = [&](int c) {
+    const auto rq = make_rsrc(qg + (size_t)c * C * Dk, rem_bytes(c, Dk));
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) rQ[i] = V8::bload(rq, vo_kq[i]);
+    const auto rv = make_rsrc(vg + (size_t)c * C * Dv, rem_bytes(c, Dv));
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) rV[i] = V8::bload(rv, vo_v[i]);
+    const int r = S - c * C;
+    const uint32_t nb = r > 0 ? (uint32_t)r * 4u : 0u;
+    rg = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
+    rb_ = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
+  };
+  auto st_k = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) rK[i].store(sK[slot] + lo_kq[i]);
+  };
+  auto st_tp = [&](T* dst, V8* src) {
+    src[0].store(dst + lo_tp[0]);
+    if (w == kWaves) src[1].store(dst + lo_tp[1]);  // the tail items sit in mover wave 0
+  };
+  auto st_qvg = [&]() {
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) rQ[i].store(sQ + lo_kq[i]);
+#pragma unroll
+    for (int i = 0; i < NVI; ++i)
+      if (mt + kMovers * i < NVT) rV[i].store(sV + lo_v[i]);
+    if (w == kWaves) {
+      sGam[lane] = wave_inclusive_scan_dpp(rg);
+      sBeta[lane] = rb_;
+    }
+  };
+  auto flush_out = [&](int c) {
+    const auto ro = make_rsrc(og + (size_t)c * C * Dv, rem_bytes(c, Dv));
+#pragma unroll
+    for (int i = 0; i < NVI; ++i)
+      if (mt + kMovers * i < NVT) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
+  };
+
+  __syncthreads();  // T / P zeroed
+  if (mover && NC > 0) {
+    ld_k(0);
+    ld_qvg(0);
+    ld_t(0);
+    st_k(0);
+    st_qvg();
+    st_tp(sT, rT);
+    ld_p(0);
+    ld_k(1);
+    ld_qvg(1);
+    ld_t(1);
+  }
+  __syncthreads();
+
+  if (mover) {
+    // The two roles run separate loops with the same barrier sequence, so the
+    // movers' load-to-store waits are counted on their own instruction stream.
+    for (int c = 0; c < NC; ++c) {
+      st_tp(sP, rP);
+      st_k((c + 1) & 1);
+      ld_p(c + 1);
+      ld_k(c + 2);
+      if (c > 0) flush_out(c - 1);
+      __syncthreads();  // end of B
+      st_qvg();
+      ld_qvg(c + 2);
+      __syncthreads();  // end of C
+      st_tp(sT, rT);
+      ld_t(c + 2);
+      __syncthreads();  // end of D
+    }
+    if (NC > 0) flush_out(NC - 1);
+    return;
+  }
+
+  const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
+  for (int c = 0; c < NC; ++c) {
+    PROF_MARK(0)
+    const T* sKc = sK[c & 1];
+    f4 oacc[NVB];
+    float GC, dt[4];
+    // ------------------------------------------------------------------- B
+    {
+      // K H -> X = beta (V - Gam K H) -> LDS; scale Gam Q H -> output accumulators
+      float Gt[4], bt[4];
+      const float gC = sGam[C - 1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lg + r;
+        const float gt = sGam[t];
+        Gt[r] = __expf(gt);
+        dt[r] = __expf(gC - gt);
+        bt[r] = sBeta[t];
+      }
+      GC = __expf(gC);
+      V8 kf[NQ], qf[NQ];
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        kf[s] = V8::load(sKc + (16 * w + lr) * LDK + 32 * s + 8 * lg);
+        qf[s] = V8::load(sQ + (16 * w + lr) * LDK + 32 * s + 8 * lg);
+      }
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        f4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+          const V8 hb = V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg);
+          kh = MM::mma(kf[s], hb, kh);
+          qh = MM::mma(qf[s], hb, qh);
+        }
+        const int cc = 16 * vb + lr;
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * lg + r;
+          x[r] = bt[r] * (to_f32<T>(sV[t * LDV + cc]) - Gt[r] * kh[r]);
+          oacc[vb][r] = scale * Gt[r] * qh[r];
+        }
+        store4<T>(sXt + cc * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
+      }
+    }
+    __syncthreads();
+    PROF_MARK(1)
+
+    // ------------------------------------------------------------------- C
+    // U = T X -> LDS as is and scaled by d_t
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < nks)
+          u = MM::mma(V8::load(sT + (16 * w + lr) * LDC + 32 * s + 8 * lg),
+                      V8::load(sXt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), u);
+      const int off = (16 * vb + lr) * LDC + 16 * w + 4 * lg;
+      store4<T>(sUt + off, u[0], u[1], u[2], u[3]);
+      store4<T>(sUd + off, dt[0] * u[0], dt[1] * u[1], dt[2] * u[2], dt[3] * u[3]);
+    }
+    __syncthreads();
+    PROF_MARK(2)
+
+    // ------------------------------------------------------------------- D
+    // O = scale Gam Q H + P U -> LDS; H' = Gam_C H + K^T (d U)
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 o = oacc[vb];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < nks)
+          o = MM::mma(V8::load(sP + (16 * w + lr) * LDC + 32 * s + 8 * lg),
+                      V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sO[(16 * w + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
+    }
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
+      f4 hc = hacc[j];
+      hc[0] *= GC; hc[1] *= GC; hc[2] *= GC; hc[3] *= GC;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        hc = MM::mma(lds_tr_frag(sKc, LDK, 32 * s, 16 * kb, lane),
+                     V8::load(sUd + (16 * vb + lr) * LDC + 32 * s + 8 * lg), hc);
+      hacc[j] = hc;
+      store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
+    }
+    __syncthreads();
+    PROF_MARK(3)
+  }
+
+
+#ifdef GDN_CTE_PROFILE
+  if (tid == 0 && p.prof) {
+    for (int i = 0; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
+  }
+#endif
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
+    const int cc = col0 + 16 * vb + lr;
+    if (cc < Dv) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 16 * kb + 4 * lg + r;
+        if (kk < Dk) stg[(size_t)kk * Dv + cc] = hacc[j][r];
+      }
+    }
+  }
+}
+
 template <typename T, int DK, int DVT>
 hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
   const int NC = (p.S + kC - 1) / kC;
@@ -665,7 +994,10 @@ hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long grid2 = (long)p.B * p.Hv * ((p.Dv + DVT - 1) / DVT);
-  hipLaunchKernelGGL((cte_state_kernel<T, DK, DVT>), dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((cte_state_ws_kernel<DK, DVT>), dim3((unsigned)grid2), dim3(kWsThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((cte_state_kernel<T, DK, DVT>), dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -130,6 +130,39 @@ template <> struct Mfma<float> {
 };
 
 // ---------------------------------------------------------------------------
+// Transposed LDS fragment read (gfx950 ds_read_b64_tr_b16).  Within each
+// 16-lane group, lane i receives element (i % 4) of the 8-byte reads of lanes
+// 4j + i / 4, j = 0..3.  So if lane L of the group reads row r + L / 4,
+// columns c + 4 (L % 4) .. +3 of a row-major 16-bit matrix, lane i gets column
+// c + i of rows r .. r + 3.  Two such reads give the 8 contraction elements of
+// an MFMA fragment whose contraction index runs down the rows:
+//   lane l -> M[r0 + 8 (l / 16) + j][c0 + l % 16], j = 0..7.
+// Requires 8-byte aligned rows (pitch * 2 % 8 == 0) and c0 % 4 == 0.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ Vec8<__bf16> lds_tr_frag(const __bf16* m, int pitch, int r0, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;
+  const __bf16* p0 = m + (r0 + 8 * g + (L >> 2)) * pitch + c0 + 4 * (L & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * pitch));
+  Vec8<__bf16> v;
+  v.u = make_uint4((uint16_t)a[0] | (uint32_t)(uint16_t)a[1] << 16, (uint16_t)a[2] | (uint32_t)(uint16_t)a[3] << 16,
+                   (uint16_t)b[0] | (uint32_t)(uint16_t)b[1] << 16, (uint16_t)b[2] | (uint32_t)(uint16_t)b[3] << 16);
+  return v;
+}
+// fp32 has no transposed read: gather the same fragment element by element
+__device__ __forceinline__ Vec8<float> lds_tr_frag(const float* m, int pitch, int r0, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;
+  const float* p = m + (r0 + 8 * g) * pitch + c0 + L;
+  Vec8<float> v;
+  v.a = make_float4(p[0], p[pitch], p[2 * pitch], p[3 * pitch]);
+  v.b = make_float4(p[4 * pitch], p[5 * pitch], p[6 * pitch], p[7 * pitch]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
 // wavefront reductions / scans (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x) {

@@ -259,7 +259,10 @@ def _check_block(gpu_out, d):
     assert np.mean(cs[:, :, -1] == rcs[:, :, -1]) >= 0.99
 
 
-@pytest.mark.parametrize("case", [(3, 256, 2, 4, 32, 32, 4), (5, 384, 1, 2, 64, 48, 3), (2, 128, 2, 2, 16, 16, 1)],
+# H = 1024 / 4096 take the fully unrolled K loops; B = 70 spans two batch tiles
+# with a ragged second one; Hv = 8 takes the vector a|b tile
+@pytest.mark.parametrize("case", [(3, 256, 2, 4, 32, 32, 4), (5, 384, 1, 2, 64, 48, 3), (2, 128, 2, 2, 16, 16, 1),
+                                  (70, 1024, 2, 8, 32, 32, 4), (17, 4096, 1, 8, 16, 24, 2)],
                          ids=lambda c: "B{}_H{}_Hk{}_Hv{}_Dk{}_Dv{}_W{}".format(*c))
 def test_block_small(gpu_lib, case):
     B, H, Hk, Hv, Dk, Dv, W = case
