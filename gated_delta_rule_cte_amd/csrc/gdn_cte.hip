@@ -40,14 +40,16 @@ constexpr int kC = 64;        // chunk length (one 16-row block per wave)
 constexpr int kNB = kC / 16;  // 16-token blocks per chunk
 
 #ifdef GDN_CTE_PROFILE
-constexpr int kProfSlots = 12;
-#define PROF_MARK(i)                                              \
-  if (tid == 0) {                                                 \
+constexpr int kProfSlots = 16;
+#define PROF_MARK_AT(i, who)                                      \
+  if (tid == (who)) {                                             \
     const unsigned long long now_ = __builtin_readcyclecounter(); \
     prof_acc[i] += now_ - prof_last;                              \
     prof_last = now_;                                             \
   }
+#define PROF_MARK(i) PROF_MARK_AT(i, 0)
 #else
+#define PROF_MARK_AT(i, who)
 #define PROF_MARK(i)
 #endif
 
@@ -770,108 +772,137 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
   for (int i = 0; i < NVI; ++i) {
     const int it = mt + kMovers * i, t = it / (DVT / 8), c8 = 8 * (it % (DVT / 8));
     vo_v[i] = (it < NVT && col0 + c8 < Dv) ? (uint32_t)(t * Dv + col0 + c8) * ES : kOOB;
-    lo_v[i] = t * LDV + c8;
+    lo_v[i] = it < NVT ? t * LDV + c8 : 0;
   }
-  V8 rK[NKQ], rQ[NKQ], rT[NTP], rP[NTP], rV[NVI];
-  float rg = 0.f, rb_ = 0.f;
+  // two register sets: the set of chunk c holds P(c) and the K, Q, V, g,
+  // beta, T of chunk c+1, so each load is issued two chunks before its store
+  struct Regs {
+    V8 K[NKQ], Q[NKQ], T[NTP], P[NTP], V[NVI];
+    float g, b;
+  };
+  Regs rs0, rs1;
 
   // descriptors of chunk c (range 0 past the last chunk: the loads read zero)
   auto rem_bytes = [&](int c, int row_elems) -> uint32_t {
     const int r = S - c * C;
     return r > 0 ? (uint32_t)r * (uint32_t)row_elems * ES : 0u;
   };
-  auto ld_k = [&](int c) {
+  auto ld_k = [&](Regs& m, int c) {
     const auto r = make_rsrc(kg + (size_t)c * C * Dk, rem_bytes(c, Dk));
 #pragma unroll
-    for (int i = 0; i < NKQ; ++i) rK[i] = V8::bload(r, vo_kq[i]);
+    for (int i = 0; i < NKQ; ++i) m.K[i] = V8::bload(r, vo_kq[i]);
   };
-  auto ld_p = [&](int c) {
+  auto ld_p = [&](Regs& m, int c) {
     const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < NC ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
-    for (int i = 0; i < NTP; ++i) rP[i] = V8::bload(r, vo_tp[i]);
+    for (int i = 0; i < NTP; ++i) m.P[i] = V8::bload(r, vo_tp[i]);
   };
-  auto ld_t = [&](int c) {
+  auto ld_t = [&](Regs& m, int c) {
     const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < NC ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
-    for (int i = 0; i < NTP; ++i) rT[i] = V8::bload(r, vo_tp[i]);
+    for (int i = 0; i < NTP; ++i) m.T[i] = V8::bload(r, vo_tp[i]);
   };
-  auto ld_qvg = [&](int c) {
+  auto ld_qvg = [&](Regs& m, int c) {
     const auto rq = make_rsrc(qg + (size_t)c * C * Dk, rem_bytes(c, Dk));
 #pragma unroll
-    for (int i = 0; i < NKQ; ++i) rQ[i] = V8::bload(rq, vo_kq[i]);
+    for (int i = 0; i < NKQ; ++i) m.Q[i] = V8::bload(rq, vo_kq[i]);
     const auto rv = make_rsrc(vg + (size_t)c * C * Dv, rem_bytes(c, Dv));
 #pragma unroll
-    for (int i = 0; i < NVI; ++i) rV[i] = V8::bload(rv, vo_v[i]);
+    for (int i = 0; i < NVI; ++i) m.V[i] = V8::bload(rv, vo_v[i]);
     const int r = S - c * C;
     const uint32_t nb = r > 0 ? (uint32_t)r * 4u : 0u;
-    rg = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
-    rb_ = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
+    m.g = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
+    m.b = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
   };
-  auto st_k = [&](int slot) {
+  auto ld_all = [&](Regs& m, int c) {  // P(c) and the rest of chunk c+1
+    ld_p(m, c);
+    ld_k(m, c + 1);
+    ld_qvg(m, c + 1);
+    ld_t(m, c + 1);
+  };
+  auto st_k = [&](const Regs& m, int slot) {
 #pragma unroll
-    for (int i = 0; i < NKQ; ++i) rK[i].store(sK[slot] + lo_kq[i]);
+    for (int i = 0; i < NKQ; ++i) m.K[i].store(sK[slot] + lo_kq[i]);
   };
-  auto st_tp = [&](T* dst, V8* src) {
+  auto st_tp = [&](T* dst, const V8* src) {
     src[0].store(dst + lo_tp[0]);
     if (w == kWaves) src[1].store(dst + lo_tp[1]);  // the tail items sit in mover wave 0
   };
-  auto st_qvg = [&]() {
+  auto st_qvg = [&](const Regs& m) {
 #pragma unroll
-    for (int i = 0; i < NKQ; ++i) rQ[i].store(sQ + lo_kq[i]);
+    for (int i = 0; i < NKQ; ++i) m.Q[i].store(sQ + lo_kq[i]);
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
-      if (mt + kMovers * i < NVT) rV[i].store(sV + lo_v[i]);
+      if (mt + kMovers * i < NVT) m.V[i].store(sV + lo_v[i]);
     if (w == kWaves) {
-      sGam[lane] = wave_inclusive_scan_dpp(rg);
-      sBeta[lane] = rb_;
+      sGam[lane] = wave_inclusive_scan_dpp(m.g);
+      sBeta[lane] = m.b;
     }
   };
+  // unconditional, so that every path issues the same vector memory
+  // instructions (exact waits): items past the tile and chunks outside
+  // [0, NC) are dropped by the range check
   auto flush_out = [&](int c) {
-    const auto ro = make_rsrc(og + (size_t)c * C * Dv, rem_bytes(c, Dv));
+    const auto ro = make_rsrc(og + (ptrdiff_t)c * C * Dv, c >= 0 ? rem_bytes(c, Dv) : 0u);
 #pragma unroll
-    for (int i = 0; i < NVI; ++i)
-      if (mt + kMovers * i < NVT) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
+    for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
+  };
+  // one chunk of mover work; m is the set of chunk c, refilled for chunk c+2
+  auto mover_chunk = [&](Regs& m, int c) {
+    PROF_MARK_AT(8, kThreads)
+    st_tp(sP, m.P);
+    st_k(m, (c + 1) & 1);
+    ld_p(m, c + 2);
+    ld_k(m, c + 3);
+    flush_out(c - 1);
+    PROF_MARK_AT(9, kThreads)
+    __syncthreads();  // end of B
+    PROF_MARK_AT(10, kThreads)
+    st_qvg(m);
+    ld_qvg(m, c + 3);
+    PROF_MARK_AT(11, kThreads)
+    __syncthreads();  // end of C
+    PROF_MARK_AT(12, kThreads)
+    st_tp(sT, m.T);
+    ld_t(m, c + 3);
+    PROF_MARK_AT(13, kThreads)
+    __syncthreads();  // end of D
+    PROF_MARK_AT(14, kThreads)
   };
 
   __syncthreads();  // T / P zeroed
   if (mover && NC > 0) {
-    ld_k(0);
-    ld_qvg(0);
-    ld_t(0);
-    st_k(0);
-    st_qvg();
-    st_tp(sT, rT);
-    ld_p(0);
-    ld_k(1);
-    ld_qvg(1);
-    ld_t(1);
+    ld_k(rs0, 0);
+    ld_qvg(rs0, 0);
+    ld_t(rs0, 0);
+    st_k(rs0, 0);
+    st_qvg(rs0);
+    st_tp(sT, rs0.T);
+    ld_all(rs0, 0);
+    ld_all(rs1, 1);
   }
   __syncthreads();
 
   if (mover) {
     // The two roles run separate loops with the same barrier sequence, so the
     // movers' load-to-store waits are counted on their own instruction stream.
-    for (int c = 0; c < NC; ++c) {
-      st_tp(sP, rP);
-      st_k((c + 1) & 1);
-      ld_p(c + 1);
-      ld_k(c + 2);
-      if (c > 0) flush_out(c - 1);
-      __syncthreads();  // end of B
-      st_qvg();
-      ld_qvg(c + 2);
-      __syncthreads();  // end of C
-      st_tp(sT, rT);
-      ld_t(c + 2);
-      __syncthreads();  // end of D
+    // an even number of chunks (the compute waves match a padding chunk with
+    // bare barriers); the padding chunk only moves zeros
+    for (int c = 0; c < NC; c += 2) {
+      mover_chunk(rs0, c);
+      mover_chunk(rs1, c + 1);
     }
-    if (NC > 0) flush_out(NC - 1);
+    flush_out(((NC + 1) & ~1) - 1);
+#ifdef GDN_CTE_PROFILE
+    if (tid == kThreads && p.prof) {
+      for (int i = 8; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
+    }
+#endif
     return;
   }
 
   const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
   for (int c = 0; c < NC; ++c) {
-    PROF_MARK(0)
     const T* sKc = sK[c & 1];
     f4 oacc[NVB];
     float GC, dt[4];
@@ -915,8 +946,9 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
         store4<T>(sXt + cc * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
-    __syncthreads();
     PROF_MARK(1)
+    __syncthreads();
+    PROF_MARK(2)
 
     // ------------------------------------------------------------------- C
     // U = T X -> LDS as is and scaled by d_t
@@ -932,8 +964,9 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
       store4<T>(sUt + off, u[0], u[1], u[2], u[3]);
       store4<T>(sUd + off, dt[0] * u[0], dt[1] * u[1], dt[2] * u[2], dt[3] * u[3]);
     }
+    PROF_MARK(3)
     __syncthreads();
-    PROF_MARK(2)
+    PROF_MARK(4)
 
     // ------------------------------------------------------------------- D
     // O = scale Gam Q H + P U -> LDS; H' = Gam_C H + K^T (d U)
@@ -960,14 +993,20 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
       hacc[j] = hc;
       store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
     }
+    PROF_MARK(0)
     __syncthreads();
-    PROF_MARK(3)
+    PROF_MARK(5)
+  }
+  if (NC & 1) {  // the movers' padding chunk
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
   }
 
 
 #ifdef GDN_CTE_PROFILE
   if (tid == 0 && p.prof) {
-    for (int i = 0; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
+    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
   }
 #endif
 #pragma unroll
