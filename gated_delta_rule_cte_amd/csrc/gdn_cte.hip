@@ -53,6 +53,17 @@ constexpr int kProfSlots = 16;
 #define PROF_MARK(i)
 #endif
 
+#ifdef GDN_CTE_PROFILE_LOCAL
+#define LPROF(i)                                                  \
+  if (tid == 0) {                                                 \
+    const unsigned long long now_ = __builtin_readcyclecounter(); \
+    lprof[i] += now_ - lprof_last;                                \
+    lprof_last = now_;                                            \
+  }
+#else
+#define LPROF(i)
+#endif
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -150,6 +161,10 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
   const int c0 = c * C, nvalid = min(C, S - c0);
   const float scale = p.scale;
 
+#ifdef GDN_CTE_PROFILE_LOCAL
+  unsigned long long lprof[8] = {};
+  unsigned long long lprof_last = __builtin_readcyclecounter();
+#endif
   // K, Q chunk tiles (all loads issued before the first store); g, beta
   {
     const T* kg = static_cast<const T*>(p.k) + ((size_t)(b * Hk + hk) * S + c0) * Dk;
@@ -179,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();
+  LPROF(0)
 
   // raw K K^T for row block w and Q K^T for row block NB-1-w (lower blocks)
   const int rk = w, rq = NB - 1 - w;
@@ -201,6 +217,7 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();  // K, Q tiles are dead from here on
+  LPROF(1)
 
   // decays: A (fp32) into the K tile's bytes, P (compute type) into the Q tile's
   {
@@ -238,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();
+  LPROF(2)
 
   // diagonal 16x16 blocks of T: lane = (block, column), forward substitution
   if (w == 0) {
@@ -263,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
   }
   __syncthreads();
+  LPROF(3)
 
   // off-diagonal blocks, one level (block distance d) at a time
 #pragma unroll
@@ -291,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     __syncthreads();
   }
 
+  LPROF(4)
   // T (lower blocks, rounded to the compute type) and P -> workspace, 16-byte stores
   T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
   T* Pg = Tg + C * C;
@@ -314,6 +334,218 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     v.store(Tg + t * C + c8);
     V8::load(sPs + t * LDC + c8).store(Pg + t * C + c8);
   }
+  LPROF(5)
+#ifdef GDN_CTE_PROFILE_LOCAL
+  if (tid == 0 && p.prof)
+    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * 16 + i] = lprof[i];
+#endif
+}
+
+// ===========================================================================
+// kernel 1, bf16: one wave per chunk
+// ===========================================================================
+// The same chunk-local products as above with no workgroup barrier: one
+// wave computes a whole chunk, so many chunks are in flight per CU.
+//  - K and Q arrive straight from HBM as MFMA fragments (16 bytes per lane).
+//  - A and P are produced transposed (the K rows of block j as the first
+//    operand), so a lane holds 4 consecutive columns of one row and writes
+//    them with one store.
+//  - Lower 16x16 blocks of A and T are kept packed in LDS (row pitch of 20
+//    floats: the row reads below hit 16 distinct bank groups).
+//  - Diagonal blocks of T by forward substitution (lane = block, column);
+//    off-diagonal blocks level by level, T_ij = -T_ii sum_m A_im T_mj, on
+//    fp32 MFMA with a permuted contraction index (16x16x4 instruction s
+//    takes index 4 (l / 16) + s): the first operand is 4 consecutive columns
+//    of a row (one LDS read), the second is the accumulator layout itself, so
+//    the partial sums and the T blocks never leave the registers.
+constexpr int kLB = 20;         // fp32 row pitch of a packed 16x16 block
+constexpr int kBlkF = 16 * kLB;  // floats per packed block
+constexpr int kPB = 24;         // bf16 row pitch of a packed P block
+constexpr int kNTri = kNB * (kNB + 1) / 2;
+
+__device__ __forceinline__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// sum over s of X[m][4 (l/16) + s] Y[4 (l/16) + s][n]: a4 = this lane's row
+// segment of X, b = Y in the accumulator layout
+__device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b[3], c, 0, 0, 0);
+  return c;
+}
+
+template <int DK>
+__global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
+  using T = __bf16;
+  using V8 = Vec8<T>;
+  using MM = Mfma<T>;
+  constexpr int C = kC, NB = kNB, NS = DK / 32;
+
+  __shared__ __align__(16) float sA[kNTri * kBlkF];  // A; P (bf16) once the inverse is done
+  __shared__ __align__(16) float sTb[kNTri * kBlkF];
+  __shared__ __align__(16) float sGam[C];
+  __shared__ __align__(16) float sBeta[C];
+
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int tid = lane;
+#ifdef GDN_CTE_PROFILE_LOCAL
+  unsigned long long lprof[8] = {};
+  unsigned long long lprof_last = __builtin_readcyclecounter();
+#endif
+  const int S = p.S, Dk = p.Dk, Hk = p.Hk, Hv = p.Hv;
+  const int NC = (S + C - 1) / C;
+  const int G = Hv / Hk;
+  const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
+  const int hh = lid % G;
+  const int c = (lid / G) % NC;
+  const int bhk = lid / (G * NC);
+  const int b = bhk / Hk, hk = bhk - b * Hk;
+  const int h = hk * G + hh;
+  const int bh = b * Hv + h;
+  const int c0 = c * C;
+  const uint32_t rem = (uint32_t)(S - c0);
+
+  // K, Q fragments of all four row blocks; g, beta (lane = token)
+  const auto rK = make_rsrc(static_cast<const T*>(p.k) + ((size_t)(b * Hk + hk) * S + c0) * Dk, rem * Dk * 2u);
+  const auto rQ = make_rsrc(static_cast<const T*>(p.q) + ((size_t)(b * Hk + hk) * S + c0) * Dk, rem * Dk * 2u);
+  V8 kf[NB][NS], qf[NB][NS];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int k8 = 32 * s + 8 * lg;
+      const uint32_t off = k8 < Dk ? (uint32_t)((16 * rb + lr) * Dk + k8) * 2u : kOOB;
+      kf[rb][s] = V8::bload(rK, off);
+      qf[rb][s] = V8::bload(rQ, off);
+    }
+  const float gl = buf_load_f32(make_rsrc(p.g + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
+  const float be = buf_load_f32(make_rsrc(p.beta + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
+  sGam[lane] = wave_inclusive_scan_dpp(gl);
+  sBeta[lane] = be;
+  wave_lds_sync();
+  LPROF(0)
+
+  // A (packed, fp32) and P (registers): lane holds row 16 i + lr, columns 16 j + 4 lg .. +3
+  const float scale = p.scale;
+  f4 pacc[kNTri];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const float gt = sGam[16 * i + lr], bt = sBeta[16 * i + lr];
+    const int t = 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      f4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        kk = MM::mma(kf[j][s], kf[i][s], kk);
+        qk = MM::mma(kf[j][s], qf[i][s], qk);
+      }
+      const float4 gs = *reinterpret_cast<const float4*>(&sGam[16 * j + 4 * lg]);
+      const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+      float a[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sc = 16 * j + 4 * lg + r;
+        const float e = __expf(gt - gsv[r]);
+        a[r] = sc < t ? bt * kk[r] * e : 0.f;
+        pacc[tri(i, j)][r] = sc <= t ? scale * qk[r] * e : 0.f;
+      }
+      *reinterpret_cast<float4*>(&sA[tri(i, j) * kBlkF + lr * kLB + 4 * lg]) = make_float4(a[0], a[1], a[2], a[3]);
+    }
+  }
+  wave_lds_sync();
+  LPROF(1)
+
+  // diagonal blocks of T: lane = (block, column), forward substitution
+  {
+    const int blk = lane >> 4, j = lane & 15;
+    const float* Ab = sA + tri(blk, blk) * kBlkF;
+    float tc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float row[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(Ab + i * kLB + 4 * q);
+        row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
+      if (i > j) tc[i] = -acc;
+    }
+    float* Tb = sTb + tri(blk, blk) * kBlkF;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Tb[i * kLB + j] = tc[i];
+  }
+  wave_lds_sync();
+  LPROF(2)
+
+  // T blocks in the accumulator layout (lane: rows 4 lg + r, column lr)
+  f4 tb[kNTri];
+#pragma unroll
+  for (int d = 0; d < NB; ++d)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tb[tri(d, d)][r] = sTb[tri(d, d) * kBlkF + (4 * lg + r) * kLB + lr];
+#pragma unroll
+  for (int d = 1; d < NB; ++d) {
+#pragma unroll
+    for (int j = 0; j + d < NB; ++j) {
+      const int i = j + d;
+      f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = j; m < i; ++m)
+        z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), tb[tri(m, j)], z);
+      const f4 tz = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, i) * kBlkF + lr * kLB + 4 * lg]), z,
+                              f4{0.f, 0.f, 0.f, 0.f});
+      tb[tri(i, j)] = -tz;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < NB; ++d)
+#pragma unroll
+    for (int j = 0; j + d < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sTb[tri(j + d, j) * kBlkF + (4 * lg + r) * kLB + lr] = tb[tri(j + d, j)][r];
+  // P (bf16) into the A area, which the levels above no longer read
+  T* sP = reinterpret_cast<T*>(sA);
+  wave_lds_sync();
+  LPROF(3)
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j <= i; ++j)
+      store4<T>(sP + tri(i, j) * 16 * kPB + lr * kPB + 4 * lg, pacc[tri(i, j)][0], pacc[tri(i, j)][1],
+                pacc[tri(i, j)][2], pacc[tri(i, j)][3]);
+  wave_lds_sync();
+
+  // lower blocks of T and P -> workspace, 16-byte stores (item: block, row, half)
+  T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
+  T* Pg = Tg + C * C;
+#pragma unroll
+  for (int q = 0; q < kNTri * 32 / kWave; ++q) {
+    const int it = lane + kWave * q;
+    const int blk = it / 32, row = (it % 32) / 2, half = it % 2;
+    const int bi = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
+    const int bj = blk - tri(bi, 0);
+    const float* src = sTb + blk * kBlkF + row * kLB + 8 * half;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    bf16x8 f;
+    f[0] = f2bf(x0.x); f[1] = f2bf(x0.y); f[2] = f2bf(x0.z); f[3] = f2bf(x0.w);
+    f[4] = f2bf(x1.x); f[5] = f2bf(x1.y); f[6] = f2bf(x1.z); f[7] = f2bf(x1.w);
+    const size_t go = (size_t)(16 * bi + row) * C + 16 * bj + 8 * half;
+    *reinterpret_cast<uint4*>(Tg + go) = __builtin_bit_cast(uint4, f);
+    *reinterpret_cast<uint4*>(Pg + go) = *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
+  }
+  LPROF(4)
+#ifdef GDN_CTE_PROFILE_LOCAL
+  if (tid == 0 && p.prof)
+    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * 16 + i] = lprof[i];
+#endif
 }
 
 // ===========================================================================
@@ -1028,7 +1260,10 @@ hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
   const int NC = (p.S + kC - 1) / kC;
   if (NC > 0) {
     const long grid1 = (long)p.B * p.Hv * NC;
-    hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((cte_local1_kernel<DK>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+    else
+      hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
