@@ -14,7 +14,14 @@ working set of consecutive calls (>= 396 MiB per entry point) exceeds the
 Each step is captured once per input set as a HIP graph (torch.cuda.CUDAGraph
 around the library's launches on the current stream), so the timed region holds
 only GPU work and no Python launch overhead.  Times come from HIP events on
-that stream.  Per-entry-point times come from graphs holding only that call.
+that stream.  Per-entry-point times come from graphs holding 16 calls of that
+entry point (input sets in rotation), so they carry no graph-launch gap and
+agree with the kernel durations rocprofv3 reports.
+
+HBM traffic per call (`traffic`) is read from profiles/traffic.json, written by
+`--record-traffic` from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over
+`--eager` and `--copy-calibration` runs; it is reported as null for an entry
+point whose sources changed since.
 
 Prints one JSON line (rank 0).  `--gpus N` with N > 1 exits: this build runs on
 one GPU.
@@ -37,10 +44,29 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2516.6      # dense MFMA, 256 CUs x 4096 flop/clk x 2.4 GHz
 CHUNK = 64                     # tokens per chunk of the bf16 prefill kernel
 
+# HBM traffic per call, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (see
+# --record-traffic); reported only while the sources it was measured on are
+# unchanged
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "gated_delta_rule_cte_amd", "csrc")
+OP_SOURCES = {
+    "cte": ["gdn_api.cpp", "gdn_cte.hip", "gdn_device.h", "gdn_launch.h"],
+    "tkg": ["gdn_api.cpp", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
+    "block": ["gdn_api.cpp", "gdn_block.hip", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
+}
+# kernels of each entry point in the bench workloads: (name fragment, grid in threads or None)
+OP_KERNELS = {
+    "cte": [("cte_local", None), ("cte_state", None)],
+    "tkg": [("tkg_kernel", 1024 * 256)],
+    "block": [("block_proj_kernel", None), ("tkg_kernel", 2048 * 256)],
+}
+COPY_CAL_BYTES = 512 << 20
+
 CTE = dict(B=1, Hk=16, Hv=32, S=4096, Dk=128, Dv=128)
 TKG = dict(B=32, Hv=32, K=128, V=128)
 BLK = dict(B=64, H=2048, Hk=16, Hv=32, Dk=128, Dv=128, K_win=4)
 NSETS = 4
+OP_REP = 16                    # calls per per-entry-point graph
 
 
 def cte_flops_per_token_head(C, Dk, Dv):
@@ -69,6 +95,68 @@ def block_bytes(B, H, Hk, Hv, Dk, Dv, K_win):
             + 2 * B * Hv * Dk * Dv * 4 + B * value_dim * 2 + 2 * Hv * 4 + Dv * 4)
 
 
+def source_digest(op):
+    import hashlib
+    h = hashlib.sha256()
+    for f in OP_SOURCES[op]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """op -> HBM bytes per call, for the ops whose sources are unchanged since the counters."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    return {op: v["bytes_per_call"] for op, v in rec.get("ops", {}).items()
+            if rec.get("sources", {}).get(op) == source_digest(op)}
+
+
+def record_traffic(d):
+    """Write profiles/traffic.json from the four rocprofv3 counter CSVs in directory d:
+    bench_{FETCH,WRITE}_SIZE (bench.py --eager) and copy_{FETCH,WRITE}_SIZE (--copy-calibration)."""
+    import csv
+
+    def per_kernel(path):
+        acc = {}
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                key = (row["Kernel_Name"], int(row["Grid_Size"]))
+                acc.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    f = per_kernel(os.path.join(d, "bench_FETCH_SIZE_counter_collection.csv"))
+    w = per_kernel(os.path.join(d, "bench_WRITE_SIZE_counter_collection.csv"))
+    cf = per_kernel(os.path.join(d, "copy_FETCH_SIZE_counter_collection.csv"))
+    cw = per_kernel(os.path.join(d, "copy_WRITE_SIZE_counter_collection.csv"))
+    ck = max((k for k in cf if "copyBuffer" in k[0]), key=lambda k: k[1])
+    known_kib = COPY_CAL_BYTES / 1024
+    ff, wf = known_kib / cf[ck], known_kib / cw[ck]
+    ops = {}
+    for op, specs in OP_KERNELS.items():
+        kern, total = {}, 0.0
+        for frag, grid in specs:
+            keys = [k for k in f if frag in k[0] and "rocclr" not in k[0] and (grid is None or k[1] == grid)]
+            if len(keys) != 1:
+                raise SystemExit(f"record-traffic: {op}: expected one kernel matching {frag!r}, found {keys}")
+            k = keys[0]
+            by = (f[k] * ff + w[k] * wf) * 1024
+            kern[k[0]] = {"grid_threads": k[1], "FETCH_SIZE_KiB": f[k], "WRITE_SIZE_KiB": w[k],
+                          "bytes_calibrated": by}
+            total += by
+        ops[op] = {"bytes_per_call": total, "kernels": kern}
+    rec = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "copy_kernel": ck[0], "FETCH_SIZE_KiB": cf[ck],
+                           "WRITE_SIZE_KiB": cw[ck], "fetch_factor": ff, "write_factor": wf},
+           "sources": {op: source_digest(op) for op in OP_SOURCES},
+           "ops": ops}
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({op: v["bytes_per_call"] for op, v in ops.items()}))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +166,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["cte", "tkg", "block"], default=None,
                     help="run only one entry point's graphs (for profiler runs)")
+    ap.add_argument("--eager", type=int, default=0, metavar="N",
+                    help="no timing: N plain calls per entry point and input set (for counter runs)")
+    ap.add_argument("--record-traffic", metavar="DIR", default=None,
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs in DIR (no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device-to-device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -85,6 +177,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the kernels shard over (batch, head) across GPUs by design, but no multi-GPU "
@@ -184,6 +279,14 @@ def main():
         for s in sets:
             fn(s)
     torch.cuda.synchronize()
+    if args.eager:
+        for name, fn, sets in ops:
+            for _ in range(args.eager):
+                for s in sets:
+                    fn(s)
+            torch.cuda.synchronize()
+        print(json.dumps({"eager_calls_per_op": args.eager * NSETS + NSETS, "ops": [n for n, _, _ in ops]}))
+        return
 
     # -------------------------------------------------------------- graphs
     stream = torch.cuda.Stream()
@@ -195,11 +298,14 @@ def main():
                 for _, fn, sets in ops:
                     fn(sets[i])
             step_graphs.append(g)
-            for name, fn, sets in ops:
-                go = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(go, stream=stream):
-                    fn(sets[i])
-                op_graphs[name].append(go)
+        # per entry point: OP_REP calls in one graph (input sets in rotation),
+        # so the time per call carries no graph-launch gap
+        for name, fn, sets in ops:
+            go = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(go, stream=stream):
+                for r in range(OP_REP):
+                    fn(sets[r % NSETS])
+            op_graphs[name].append(go)
     torch.cuda.synchronize()
 
     def timed(graphs, n):
@@ -207,7 +313,7 @@ def main():
         with torch.cuda.stream(stream):
             ev0.record(stream)
             for j in range(n):
-                graphs[j % NSETS].replay()
+                graphs[j % len(graphs)].replay()
             ev1.record(stream)
         ev1.synchronize()
         return ev0.elapsed_time(ev1) / n  # ms per replay
@@ -222,8 +328,9 @@ def main():
 
     per_op_ms = {}
     for name, _, _ in ops:
-        timed(op_graphs[name], 10)
-        per_op_ms[name] = timed(op_graphs[name], args.op_iters)
+        timed(op_graphs[name], 1)
+        reps = max(1, args.op_iters // OP_REP)
+        per_op_ms[name] = timed(op_graphs[name], reps) / OP_REP
 
     # ---------------------------------------------------------- rooflines
     rooflines = {}
@@ -249,6 +356,9 @@ def main():
         rooflines["block"] = dict(bound="hbm", achieved=by / t / 1e9, peak=PEAK_HBM_GBS, unit="GB/s",
                                   frac=by / t / 1e9 / PEAK_HBM_GBS, traffic=None, algorithmic_bytes=by,
                                   us=t * 1e6, kernels=2)
+    traffic = load_traffic()
+    for op, r in rooflines.items():
+        r["traffic"] = traffic.get(op)
     dominant = max(per_op_ms, key=per_op_ms.get)
 
     # ------------------------------------------------------- CPU baseline
@@ -282,7 +392,8 @@ def main():
                          "gdn_tkg BH=1024 K=V=128 + gdn_block_tkg B=64 H=2048 Hk=16 Hv=32 D=128 K_win=4"),
             "prefill_tokens_per_step": CTE["B"] * CTE["S"],
             "input_sets_rotated": NSETS,
-            "timing": "HIP graphs replayed on one stream, HIP events",
+            "timing": ("HIP graphs replayed on one stream, HIP events; a step is one graph (all three "
+                       "entry points), per-entry-point times come from graphs of 16 calls"),
         },
         "roofline": dict(rooflines[dominant], kernel={"cte": "cte_kernel", "tkg": "tkg_kernel",
                                                       "block": "block_proj_kernel + tkg_kernel"}[dominant]),

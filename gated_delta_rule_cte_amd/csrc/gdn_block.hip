@@ -75,7 +75,12 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
   const int nkt = NKT > 0 ? NKT : H / kBK;
 
   // column tile -> (matrix, first column); the a|b tile reads W_in_a then W_in_b
-  int tile = blockIdx.x, seg, ncols;
+  // neighbouring column tiles read neighbouring bytes of every weight row
+  // (halves of the same 128-byte lines): keep them on one XCD
+  const int nblk = (int)(gridDim.x * gridDim.y);
+  const int lid = xcd_logical_id((int)(blockIdx.x + blockIdx.y * gridDim.x), nblk);
+  const int mblk = lid / (int)gridDim.x;
+  int tile = lid - mblk * (int)gridDim.x, seg, ncols;
   if (tile < nt_qkv) {
     seg = 0; ncols = conv_dim;
   } else if ((tile -= nt_qkv) < nt_z) {
@@ -84,7 +89,7 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
     tile -= nt_z; seg = 2; ncols = 2 * p.Hv;
   }
   const int n0 = tile * kBN;
-  const int m0 = blockIdx.y * kBM;
+  const int m0 = mblk * kBM;
 
   // Branch-free loads: each element's buffer offset is loop invariant except
   // for the K-tile step, and masked-off elements (columns past the matrix,
@@ -244,7 +249,9 @@ __global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams 
   __shared__ __align__(16) __bf16 sW[kBK * kLDW];
   const int conv_dim = 2 * p.Hk * p.Dk + p.Hv * p.Dv;
   const int nt_main = (conv_dim + kBN - 1) / kBN + (p.Hv * p.Dv + kBN - 1) / kBN;
-  if ((int)blockIdx.x < nt_main)
+  const int nblk = (int)(gridDim.x * gridDim.y);
+  const int lid = xcd_logical_id((int)(blockIdx.x + blockIdx.y * gridDim.x), nblk);
+  if (lid % (int)gridDim.x < nt_main)
     block_proj_body<kSingle, NKT>(p, sH, sW);
   else if (p.Hv % 8 == 0)
     block_proj_body<kAB, NKT>(p, sH, sW);

@@ -96,16 +96,6 @@ __device__ __forceinline__ void store2<__bf16>(__bf16* p, float a, float b) {
   *reinterpret_cast<uint32_t*>(p) = lo | (hi << 16);
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i % 8), and each XCD has its own L2.  This remap gives XCD x the
-// contiguous logical ids [x n/8, (x+1) n/8), so workgroups that read the same
-// tiles (neighbouring logical ids) share one L2.  Identity when n % 8 != 0.
-constexpr int kXCDs = 8;
-__device__ __forceinline__ int xcd_logical_id(int hw_id, int n) {
-  if (n % kXCDs != 0) return hw_id;
-  return (hw_id % kXCDs) * (n / kXCDs) + hw_id / kXCDs;
-}
-
 // T (bf16 or fp32) workspace of one (batch*value head, chunk): T then P, each [C][C]
 template <typename T>
 __device__ __forceinline__ T* ws_chunk(void* ws, int bh, int NC, int c) {

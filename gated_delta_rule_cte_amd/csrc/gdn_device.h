@@ -163,6 +163,20 @@ __device__ __forceinline__ Vec8<float> lds_tr_frag(const float* m, int pitch, in
 }
 
 // ---------------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (linear workgroup id i
+// runs on XCD i % 8), and each XCD has its own L2.  This remap gives XCD x a
+// contiguous range of logical ids (n / 8 of them, one more for the first
+// n % 8 XCDs), so workgroups that read the same bytes (neighbouring logical
+// ids) share one L2.  A bijection on [0, n) for every n.
+// ---------------------------------------------------------------------------
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int xcd_logical_id(int hw_id, int n) {
+  const int q = n / kXCDs, r = n % kXCDs;
+  const int x = hw_id % kXCDs, slot = hw_id / kXCDs;
+  return x * q + (x < r ? x : r) + slot;
+}
+
+// ---------------------------------------------------------------------------
 // wavefront reductions / scans (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x) {
