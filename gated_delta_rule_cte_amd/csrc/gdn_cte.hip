@@ -882,12 +882,10 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
 //   barrier
 // Only the lower 16x16 blocks of T and P are moved; their upper blocks are
 // zeroed once and never written again.
-constexpr int kWsThreads = 512;
-constexpr int kMovers = kWsThreads - kThreads;  // mover threads
 constexpr int kTriItems = (kNB * (kNB + 1) / 2) * 16 * 2;  // 16-byte items in the lower blocks of a C x C tile
 
-template <int DK, int DVT>
-__global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParams p) {
+template <int DK, int DVT, int MW>
+__global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
   using MM = Mfma<T>;
@@ -900,13 +898,15 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
   constexpr int HPW = NKB * NVB / kWaves;                // state blocks per compute wave
   constexpr int NQ = DK / 32;                            // Q / K fragments per lane
   constexpr int KSTEPS = C / 32;
+  constexpr int kMovers = MW * kWave;                    // mover threads
+  constexpr int kAll = (kWaves + MW) * kWave;
   constexpr int NKQ = C * (DK / 8) / kMovers;            // K or Q items per mover thread
   constexpr int NTP = (kTriItems + kMovers - 1) / kMovers;
   constexpr int NVT = C * (DVT / 8);                     // V / O items
   constexpr int NVI = (NVT + kMovers - 1) / kMovers;
   constexpr uint32_t ES = 2;
   static_assert(NKB * NVB % kWaves == 0 && NKQ * kMovers == C * (DK / 8), "tile split");
-  static_assert(NTP == 2 && kTriItems - kMovers <= kWave, "second T/P item belongs to mover wave 0 only");
+  static_assert(kTriItems % kWave == 0 && NVT % kWave == 0, "T/P and V items end on a wave boundary");
 
   __shared__ __align__(16) T sK[2][C * LDK];
   __shared__ __align__(16) T sQ[C * LDK];
@@ -918,8 +918,9 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
   __shared__ __align__(16) T sUt[DVT * LDC];
   __shared__ __align__(16) T sUd[DVT * LDC];
   __shared__ __align__(16) T sO[C * LDV];
-  __shared__ float sGam[C];
-  __shared__ float sBeta[C];
+  __shared__ __align__(16) float sEG[C];   // exp(gam_t)
+  __shared__ __align__(16) float sED[C];   // exp(gam_C - gam_t)
+  __shared__ __align__(16) float sBeta[C];
 
   const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
   const int lr = lane & 15, lg = lane >> 4;
@@ -945,7 +946,7 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
   float* stg = p.state + (size_t)bh * Dk * Dv;
 
   // upper blocks of T and P read as zero for good
-  for (int i = tid; i < C * LDC / 2; i += kWsThreads) {
+  for (int i = tid; i < C * LDC / 2; i += kAll) {
     reinterpret_cast<uint32_t*>(sT)[i] = 0u;
     reinterpret_cast<uint32_t*>(sP)[i] = 0u;
   }
@@ -988,7 +989,7 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
     const int cb = bi - rb * (rb + 1) / 2;
     const int row = 16 * rb + (it % 32) / 2, col = 16 * cb + 8 * (it % 2);
     vo_tp[i] = it < kTriItems ? (uint32_t)(row * C + col) * ES : kOOB;
-    lo_tp[i] = row * LDC + col;
+    lo_tp[i] = it < kTriItems ? row * LDC + col : 0;
   }
 #pragma unroll
   for (int i = 0; i < NVI; ++i) {
@@ -1047,17 +1048,23 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
     for (int i = 0; i < NKQ; ++i) m.K[i].store(sK[slot] + lo_kq[i]);
   };
   auto st_tp = [&](T* dst, const V8* src) {
-    src[0].store(dst + lo_tp[0]);
-    if (w == kWaves) src[1].store(dst + lo_tp[1]);  // the tail items sit in mover wave 0
+#pragma unroll
+    for (int i = 0; i < NTP; ++i)
+      if (mt + kMovers * i < kTriItems) src[i].store(dst + lo_tp[i]);  // wave-uniform
   };
-  auto st_qvg = [&](const Regs& m) {
+  auto st_q = [&](const Regs& m) {
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) m.Q[i].store(sQ + lo_kq[i]);
+  };
+  auto st_vg = [&](const Regs& m) {
 #pragma unroll
     for (int i = 0; i < NVI; ++i)
       if (mt + kMovers * i < NVT) m.V[i].store(sV + lo_v[i]);
     if (w == kWaves) {
-      sGam[lane] = wave_inclusive_scan_dpp(m.g);
+      const float gam = wave_inclusive_scan_dpp(m.g);
+      const float gamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), C - 1));
+      sEG[lane] = __expf(gam);
+      sED[lane] = __expf(gamC - gam);
       sBeta[lane] = m.b;
     }
   };
@@ -1070,23 +1077,62 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
     for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
   };
   // one chunk of mover work; m is the set of chunk c, refilled for chunk c+2
+  // The outputs are computed by the movers, off the state chain: mover wave
+  // mw owns rows 16 mw .. +15.  scale Gam Q H while the compute waves run B
+  // (Q and H of chunk c are both in LDS then), + P U once U is there.
+  // with eight movers the last four compute the outputs
+  const int mw = w - kWaves - (MW - kWaves);
+  const int mnks = (16 * (mw + 1) + 31) / 32;  // k-steps of P touching lower blocks
+  auto out_qh = [&](f4* oacc, float4 eg) {
+    const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
+    V8 qf[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) qf[s] = V8::load(sQ + (16 * mw + lr) * LDK + 32 * s + 8 * lg);
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 qh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) qh = MM::mma(qf[s], V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg), qh);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[vb][r] = scale * egv[r] * qh[r];
+    }
+  };
+  auto out_pu = [&](f4* oacc) {
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      f4 o = oacc[vb];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        if (s < mnks)
+          o = MM::mma(V8::load(sP + (16 * mw + lr) * LDC + 32 * s + 8 * lg),
+                      V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sO[(16 * mw + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
+    }
+  };
   auto mover_chunk = [&](Regs& m, int c) {
     PROF_MARK_AT(8, kThreads)
     st_tp(sP, m.P);
     st_k(m, (c + 1) & 1);
+    PROF_MARK_AT(15, kThreads)
     ld_p(m, c + 2);
     ld_k(m, c + 3);
+    PROF_MARK_AT(6, kThreads)
     flush_out(c - 1);
+    f4 oacc[NVB];
+    if (mw >= 0) out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]));
     PROF_MARK_AT(9, kThreads)
     __syncthreads();  // end of B
     PROF_MARK_AT(10, kThreads)
-    st_qvg(m);
+    st_q(m);
+    st_vg(m);
     ld_qvg(m, c + 3);
     PROF_MARK_AT(11, kThreads)
     __syncthreads();  // end of C
     PROF_MARK_AT(12, kThreads)
     st_tp(sT, m.T);
     ld_t(m, c + 3);
+    if (mw >= 0) out_pu(oacc);
     PROF_MARK_AT(13, kThreads)
     __syncthreads();  // end of D
     PROF_MARK_AT(14, kThreads)
@@ -1098,7 +1144,8 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
     ld_qvg(rs0, 0);
     ld_t(rs0, 0);
     st_k(rs0, 0);
-    st_qvg(rs0);
+    st_q(rs0);
+    st_vg(rs0);
     st_tp(sT, rs0.T);
     ld_all(rs0, 0);
     ld_all(rs1, 1);
@@ -1118,6 +1165,7 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
 #ifdef GDN_CTE_PROFILE
     if (tid == kThreads && p.prof) {
       for (int i = 8; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
+    p.prof[(size_t)blockIdx.x * kProfSlots + 6] = prof_acc[6];
     }
 #endif
     return;
@@ -1126,46 +1174,29 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
   const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
   for (int c = 0; c < NC; ++c) {
     const T* sKc = sK[c & 1];
-    f4 oacc[NVB];
     float GC, dt[4];
     // ------------------------------------------------------------------- B
     {
-      // K H -> X = beta (V - Gam K H) -> LDS; scale Gam Q H -> output accumulators
-      float Gt[4], bt[4];
-      const float gC = sGam[C - 1];
+      // K H -> X = beta (V - Gam K H) -> LDS
+      const float4 eg = *reinterpret_cast<const float4*>(&sEG[16 * w + 4 * lg]);
+      const float4 ed = *reinterpret_cast<const float4*>(&sED[16 * w + 4 * lg]);
+      const float4 be = *reinterpret_cast<const float4*>(&sBeta[16 * w + 4 * lg]);
+      const float Gt[4] = {eg.x, eg.y, eg.z, eg.w}, bt[4] = {be.x, be.y, be.z, be.w};
+      dt[0] = ed.x; dt[1] = ed.y; dt[2] = ed.z; dt[3] = ed.w;
+      GC = sEG[C - 1];
+      V8 kf[NQ];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lg + r;
-        const float gt = sGam[t];
-        Gt[r] = __expf(gt);
-        dt[r] = __expf(gC - gt);
-        bt[r] = sBeta[t];
-      }
-      GC = __expf(gC);
-      V8 kf[NQ], qf[NQ];
-#pragma unroll
-      for (int s = 0; s < NQ; ++s) {
-        kf[s] = V8::load(sKc + (16 * w + lr) * LDK + 32 * s + 8 * lg);
-        qf[s] = V8::load(sQ + (16 * w + lr) * LDK + 32 * s + 8 * lg);
-      }
+      for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sKc + (16 * w + lr) * LDK + 32 * s + 8 * lg);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        f4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
+        f4 kh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-          const V8 hb = V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg);
-          kh = MM::mma(kf[s], hb, kh);
-          qh = MM::mma(qf[s], hb, qh);
-        }
-        const int cc = 16 * vb + lr;
+        for (int s = 0; s < NQ; ++s) kh = MM::mma(kf[s], V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg), kh);
+        const uint2 v4 = lds_tr4(sV, LDV, 16 * w + 4 * lg, 16 * vb, lane);  // V[16 w + 4 lg + r][16 vb + lr]
         float x[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w + 4 * lg + r;
-          x[r] = bt[r] * (to_f32<T>(sV[t * LDV + cc]) - Gt[r] * kh[r]);
-          oacc[vb][r] = scale * Gt[r] * qh[r];
-        }
-        store4<T>(sXt + cc * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
+        for (int r = 0; r < 4; ++r) x[r] = bt[r] * (bf4_get(v4, r) - Gt[r] * kh[r]);
+        store4<T>(sXt + (16 * vb + lr) * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
     PROF_MARK(1)
@@ -1191,18 +1222,7 @@ __global__ __launch_bounds__(kWsThreads) void cte_state_ws_kernel(const CteParam
     PROF_MARK(4)
 
     // ------------------------------------------------------------------- D
-    // O = scale Gam Q H + P U -> LDS; H' = Gam_C H + K^T (d U)
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f4 o = oacc[vb];
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        if (s < nks)
-          o = MM::mma(V8::load(sP + (16 * w + lr) * LDC + 32 * s + 8 * lg),
-                      V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sO[(16 * w + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
-    }
+    // H' = Gam_C H + K^T (d U)
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
@@ -1258,8 +1278,14 @@ hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long grid2 = (long)p.B * p.Hv * ((p.Dv + DVT - 1) / DVT);
+#ifndef GDN_CTE_MOVER_WAVES
+  constexpr int MW = 4;
+#else
+  constexpr int MW = GDN_CTE_MOVER_WAVES;
+#endif
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((cte_state_ws_kernel<DK, DVT>), dim3((unsigned)grid2), dim3(kWsThreads), 0, stream, p);
+    hipLaunchKernelGGL((cte_state_ws_kernel<DK, DVT, MW>), dim3((unsigned)grid2), dim3((kWaves + MW) * kWave), 0,
+                       stream, p);
   else
     hipLaunchKernelGGL((cte_state_kernel<T, DK, DVT>), dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

@@ -152,6 +152,21 @@ __device__ __forceinline__ Vec8<__bf16> lds_tr_frag(const __bf16* m, int pitch, 
                    (uint16_t)b[0] | (uint32_t)(uint16_t)b[1] << 16, (uint16_t)b[2] | (uint32_t)(uint16_t)b[3] << 16);
   return v;
 }
+// One transposed read on its own: lane l of group g = l / 16 reads row
+// row0 + l % 16 / 4 (row0 may depend on g), columns c0 + 4 (l % 4) .. +3, and
+// receives M[row0 + j][c0 + l % 16], j = 0..3, as 4 packed bf16.
+__device__ __forceinline__ uint2 lds_tr4(const __bf16* m, int pitch, int row0, int c0, int lane) {
+  const int L = lane & 15;
+  const i16x4 a =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(m + (row0 + (L >> 2)) * pitch + c0 + 4 * (L & 3)));
+  return make_uint2((uint16_t)a[0] | (uint32_t)(uint16_t)a[1] << 16, (uint16_t)a[2] | (uint32_t)(uint16_t)a[3] << 16);
+}
+// element j of 4 packed bf16, as float
+__device__ __forceinline__ float bf4_get(uint2 v, int j) {
+  const uint32_t w = j < 2 ? v.x : v.y;
+  return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
 // fp32 has no transposed read: gather the same fragment element by element
 __device__ __forceinline__ Vec8<float> lds_tr_frag(const float* m, int pitch, int r0, int c0, int lane) {
   const int L = lane & 15, g = lane >> 4;
