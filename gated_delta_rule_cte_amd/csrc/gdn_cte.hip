@@ -906,12 +906,11 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   constexpr int NVI = (NVT + kMovers - 1) / kMovers;
   constexpr uint32_t ES = 2;
   static_assert(NKB * NVB % kWaves == 0 && NKQ * kMovers == C * (DK / 8), "tile split");
-  static_assert(kTriItems % kWave == 0 && NVT % kWave == 0, "T/P and V items end on a wave boundary");
+  static_assert(kTriItems % kWave == 0 && NVT % kWave == 0, "T and V items end on a wave boundary");
+  static_assert(MW == kWaves, "mover wave mw holds the Q and P rows of row block mw");
 
   __shared__ __align__(16) T sK[2][C * LDK];
-  __shared__ __align__(16) T sQ[C * LDK];
   __shared__ __align__(16) T sT[C * LDC];
-  __shared__ __align__(16) T sP[C * LDC];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
   __shared__ __align__(16) T sXt[DVT * LDC];
@@ -945,11 +944,8 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   T* og = static_cast<T*>(p.out) + (size_t)bh * S * Dv;
   float* stg = p.state + (size_t)bh * Dk * Dv;
 
-  // upper blocks of T and P read as zero for good
-  for (int i = tid; i < C * LDC / 2; i += kAll) {
-    reinterpret_cast<uint32_t*>(sT)[i] = 0u;
-    reinterpret_cast<uint32_t*>(sP)[i] = 0u;
-  }
+  // upper blocks of T read as zero for good
+  for (int i = tid; i < C * LDC / 2; i += kAll) reinterpret_cast<uint32_t*>(sT)[i] = 0u;
 
   f4 hacc[HPW];
   if (!mover) {
@@ -997,10 +993,26 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     vo_v[i] = (it < NVT && col0 + c8 < Dv) ? (uint32_t)(t * Dv + col0 + c8) * ES : kOOB;
     lo_v[i] = it < NVT ? t * LDV + c8 : 0;
   }
-  // two register sets: the set of chunk c holds P(c) and the K, Q, V, g,
-  // beta, T of chunk c+1, so each load is issued two chunks before its store
+  // The outputs are computed by the movers, off the state chain: mover wave
+  // mw owns rows 16 mw .. +15 and holds their Q and P fragments (the MFMA
+  // first operand) in registers, loaded straight from HBM.
+  const int mw = w - kWaves;
+  const int mnks = (16 * (mw + 1) + 31) / 32;  // k-steps of P touching lower blocks
+  uint32_t vo_qf[NQ], vo_pf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const int k8 = 32 * s + 8 * lg;
+    vo_qf[s] = k8 < Dk ? (uint32_t)((16 * mw + lr) * Dk + k8) * ES : kOOB;
+  }
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int k8 = 32 * s + 8 * lg;  // upper blocks read as zero
+    vo_pf[s] = (s < mnks && (k8 >> 4) <= mw) ? (uint32_t)((16 * mw + lr) * C + k8) * ES : kOOB;
+  }
+  // two register sets: the set of chunk c holds Q(c), P(c) and the K, V, g,
+  // beta, T of chunk c+1, so each load is issued two chunks before its use
   struct Regs {
-    V8 K[NKQ], Q[NKQ], T[NTP], P[NTP], V[NVI];
+    V8 K[NKQ], Qf[NQ], Pf[KSTEPS], T[NTP], V[NVI];
     float g, b;
   };
   Regs rs0, rs1;
@@ -1018,17 +1030,19 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   auto ld_p = [&](Regs& m, int c) {
     const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < NC ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
-    for (int i = 0; i < NTP; ++i) m.P[i] = V8::bload(r, vo_tp[i]);
+    for (int s = 0; s < KSTEPS; ++s) m.Pf[s] = V8::bload(r, vo_pf[s]);
+  };
+  auto ld_q = [&](Regs& m, int c) {
+    const auto r = make_rsrc(qg + (size_t)c * C * Dk, rem_bytes(c, Dk));
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) m.Qf[s] = V8::bload(r, vo_qf[s]);
   };
   auto ld_t = [&](Regs& m, int c) {
     const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < NC ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
     for (int i = 0; i < NTP; ++i) m.T[i] = V8::bload(r, vo_tp[i]);
   };
-  auto ld_qvg = [&](Regs& m, int c) {
-    const auto rq = make_rsrc(qg + (size_t)c * C * Dk, rem_bytes(c, Dk));
-#pragma unroll
-    for (int i = 0; i < NKQ; ++i) m.Q[i] = V8::bload(rq, vo_kq[i]);
+  auto ld_vg = [&](Regs& m, int c) {
     const auto rv = make_rsrc(vg + (size_t)c * C * Dv, rem_bytes(c, Dv));
 #pragma unroll
     for (int i = 0; i < NVI; ++i) m.V[i] = V8::bload(rv, vo_v[i]);
@@ -1037,10 +1051,11 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     m.g = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
     m.b = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
   };
-  auto ld_all = [&](Regs& m, int c) {  // P(c) and the rest of chunk c+1
+  auto ld_all = [&](Regs& m, int c) {  // Q(c), P(c) and the rest of chunk c+1
     ld_p(m, c);
+    ld_q(m, c);
     ld_k(m, c + 1);
-    ld_qvg(m, c + 1);
+    ld_vg(m, c + 1);
     ld_t(m, c + 1);
   };
   auto st_k = [&](const Regs& m, int slot) {
@@ -1051,10 +1066,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
     for (int i = 0; i < NTP; ++i)
       if (mt + kMovers * i < kTriItems) src[i].store(dst + lo_tp[i]);  // wave-uniform
-  };
-  auto st_q = [&](const Regs& m) {
-#pragma unroll
-    for (int i = 0; i < NKQ; ++i) m.Q[i].store(sQ + lo_kq[i]);
   };
   auto st_vg = [&](const Regs& m) {
 #pragma unroll
@@ -1076,18 +1087,8 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
     for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
   };
-  // one chunk of mover work; m is the set of chunk c, refilled for chunk c+2
-  // The outputs are computed by the movers, off the state chain: mover wave
-  // mw owns rows 16 mw .. +15.  scale Gam Q H while the compute waves run B
-  // (Q and H of chunk c are both in LDS then), + P U once U is there.
-  // with eight movers the last four compute the outputs
-  const int mw = w - kWaves - (MW - kWaves);
-  const int mnks = (16 * (mw + 1) + 31) / 32;  // k-steps of P touching lower blocks
-  auto out_qh = [&](f4* oacc, float4 eg) {
+  auto out_qh = [&](f4* oacc, float4 eg, const V8* qf) {
     const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
-    V8 qf[NQ];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) qf[s] = V8::load(sQ + (16 * mw + lr) * LDK + 32 * s + 8 * lg);
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f4 qh = {0.f, 0.f, 0.f, 0.f};
@@ -1097,66 +1098,62 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       for (int r = 0; r < 4; ++r) oacc[vb][r] = scale * egv[r] * qh[r];
     }
   };
-  auto out_pu = [&](f4* oacc) {
+  auto out_pu = [&](f4* oacc, const V8* pf) {
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f4 o = oacc[vb];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        if (s < mnks)
-          o = MM::mma(V8::load(sP + (16 * mw + lr) * LDC + 32 * s + 8 * lg),
-                      V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
+        if (s < mnks) o = MM::mma(pf[s], V8::load(sUt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), o);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sO[(16 * mw + 4 * lg + r) * LDV + 16 * vb + lr] = from_f32<T>(o[r]);
     }
   };
+  // one chunk of mover work; m is the set of chunk c, refilled for chunk c+2.
+  // scale Gam Q H while the compute waves run B (H of chunk c is in LDS
+  // then), + P U once U is there.
   auto mover_chunk = [&](Regs& m, int c) {
     PROF_MARK_AT(8, kThreads)
-    st_tp(sP, m.P);
     st_k(m, (c + 1) & 1);
-    PROF_MARK_AT(15, kThreads)
-    ld_p(m, c + 2);
     ld_k(m, c + 3);
-    PROF_MARK_AT(6, kThreads)
+    PROF_MARK_AT(15, kThreads)
     flush_out(c - 1);
     f4 oacc[NVB];
-    if (mw >= 0) out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]));
+    out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]), m.Qf);
+    ld_q(m, c + 2);
     PROF_MARK_AT(9, kThreads)
     __syncthreads();  // end of B
     PROF_MARK_AT(10, kThreads)
-    st_q(m);
     st_vg(m);
-    ld_qvg(m, c + 3);
+    ld_vg(m, c + 3);
     PROF_MARK_AT(11, kThreads)
     __syncthreads();  // end of C
     PROF_MARK_AT(12, kThreads)
     st_tp(sT, m.T);
     ld_t(m, c + 3);
-    if (mw >= 0) out_pu(oacc);
+    out_pu(oacc, m.Pf);
+    ld_p(m, c + 2);
     PROF_MARK_AT(13, kThreads)
     __syncthreads();  // end of D
     PROF_MARK_AT(14, kThreads)
   };
 
-  __syncthreads();  // T / P zeroed
-  if (mover && NC > 0) {
+  if (mover) {
+    // The two roles run separate code from here on, with the same barrier
+    // sequence, so the load-to-use waits of each are counted on its own
+    // instruction stream.
+    __syncthreads();  // T zeroed, initial state staged
     ld_k(rs0, 0);
-    ld_qvg(rs0, 0);
+    ld_vg(rs0, 0);
     ld_t(rs0, 0);
     st_k(rs0, 0);
-    st_q(rs0);
     st_vg(rs0);
     st_tp(sT, rs0.T);
     ld_all(rs0, 0);
     ld_all(rs1, 1);
-  }
-  __syncthreads();
-
-  if (mover) {
-    // The two roles run separate loops with the same barrier sequence, so the
-    // movers' load-to-store waits are counted on their own instruction stream.
-    // an even number of chunks (the compute waves match a padding chunk with
-    // bare barriers); the padding chunk only moves zeros
+    __syncthreads();  // chunk 0 staged
+    // an even number of chunks: the padding chunk of an odd count only moves
+    // zeros
     for (int c = 0; c < NC; c += 2) {
       mover_chunk(rs0, c);
       mover_chunk(rs1, c + 1);
@@ -1171,8 +1168,13 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     return;
   }
 
+  __syncthreads();  // T zeroed, initial state staged
+  __syncthreads();  // chunk 0 staged
   const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
-  for (int c = 0; c < NC; ++c) {
+  // A padding chunk past the end (odd NC) is computed like any other: its
+  // operands are zeros, exp(gam) = 1 and beta = 0, so the state is unchanged
+  // and its outputs fall outside the range check.
+  auto compute_chunk = [&](int c) {
     const T* sKc = sK[c & 1];
     float GC, dt[4];
     // ------------------------------------------------------------------- B
@@ -1238,11 +1240,10 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     PROF_MARK(0)
     __syncthreads();
     PROF_MARK(5)
-  }
-  if (NC & 1) {  // the movers' padding chunk
-    __syncthreads();
-    __syncthreads();
-    __syncthreads();
+  };
+  for (int c = 0; c < NC; c += 2) {
+    compute_chunk(c);
+    compute_chunk(c + 1);
   }
 
 
