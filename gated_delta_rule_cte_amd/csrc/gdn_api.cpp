@@ -243,8 +243,10 @@ int gdn_block_tkg(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   const size_t key_dim = (size_t)Hk * Dk, value_dim = (size_t)Hv * Dv;
   const size_t conv_dim = 2 * key_dim + value_dim;
   // weights and the hidden batch are addressed with 32-bit buffer offsets below 2^31
-  if ((size_t)H * conv_dim * 2 >= ((size_t)1 << 31) || (size_t)B * H * 2 >= ((size_t)1 << 31))
-    return fail(GDN_ERR_SHAPE, "H=%d x conv_dim=%zu weights (or the hidden batch) exceed 2 GiB", H, conv_dim);
+  if ((size_t)H * conv_dim * 2 >= ((size_t)1 << 31) || (size_t)B * H * 2 >= ((size_t)1 << 31) ||
+      (size_t)B * conv_dim * K_win * 2 >= ((size_t)1 << 31))
+    return fail(GDN_ERR_SHAPE, "H=%d x conv_dim=%zu weights (or the hidden batch, or the conv state) exceed 2 GiB",
+                H, conv_dim);
   const Span sh{"hidden", hidden, (size_t)B * H * 2}, swq{"W_in_qkv", W_in_qkv, (size_t)H * conv_dim * 2},
       swz{"W_in_z", W_in_z, (size_t)H * value_dim * 2}, swa{"W_in_a", W_in_a, (size_t)H * Hv * 2},
       swb{"W_in_b", W_in_b, (size_t)H * Hv * 2}, scw{"conv_weight", conv_weight, conv_dim * K_win * 4},

@@ -164,6 +164,26 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
 #pragma unroll
   for (int nb = 0; nb < kBN / 16; ++nb) acc[nb] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // Conv operands of the epilogue (q|k|v tiles with a 4-tap window), issued
+  // before the K loop so their latency hides behind it: the 8-byte window of
+  // each output element and the lane column's 4 taps.  Branch-free: other
+  // tiles and masked elements read zero through the range check.
+  const bool conv4 = kKind == kSingle && seg == 0 && p.K_win == 4;
+  const __amdgpu_buffer_rsrc_t rCS = make_rsrc(p.conv_state_in, (uint32_t)((size_t)B * conv_dim * 8));
+  const __amdgpu_buffer_rsrc_t rCW = make_rsrc(p.conv_weight, (uint32_t)((size_t)conv_dim * 16));
+  uint2 cwin[kBN / 16][4];
+  uint4 ctap[kBN / 16];
+#pragma unroll
+  for (int nb = 0; nb < kBN / 16; ++nb) {
+    const int nn = n0 + 16 * nb + lr;
+    ctap[nb] = buf_load16(rCW, (conv4 && nn < ncols) ? (uint32_t)nn * 16u : kOOB);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * w + 4 * lg + r;
+      cwin[nb][r] = buf_load8(rCS, (conv4 && nn < ncols && m < B) ? (uint32_t)(m * conv_dim + nn) * 8u : kOOB);
+    }
+  }
+
   Ring ring[kRing];
 #pragma unroll
   for (int u = 0; u < kRing; ++u) load(ring[u], u);
@@ -220,7 +240,19 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
       const int m = m0 + 16 * w + 4 * lg + r;
       if (m >= B) continue;
       const __bf16 y = f2bf(acc[nb][r]);
-      if (seg == 0) {
+      if (conv4) {
+        // window [state[1..3], y]; taps in fp32
+        const uint2 st = cwin[nb][r];
+        const uint32_t yb = __builtin_bit_cast(uint16_t, y);
+        const uint2 wn = make_uint2(__builtin_amdgcn_perm(st.y, st.x, 0x05040302u),
+                                    __builtin_amdgcn_perm(yb, st.y, 0x05040302u));
+        const float4 cw = __builtin_bit_cast(float4, ctap[nb]);
+        const float sum = cw.x * __uint_as_float(wn.x << 16) + cw.y * __uint_as_float(wn.x & 0xFFFF0000u) +
+                          cw.z * __uint_as_float(wn.y << 16) + cw.w * __uint_as_float(wn.y & 0xFFFF0000u);
+        buf_store8(wn, make_rsrc(p.conv_state_out, (uint32_t)((size_t)B * conv_dim * 8)),
+                   (uint32_t)(m * conv_dim + nn) * 8u);
+        static_cast<__bf16*>(p.ws_conv_out)[(size_t)m * conv_dim + nn] = f2bf(sum * sigmoidf_(sum));
+      } else if (seg == 0) {
         const int KW = p.K_win;
         const __bf16* st = static_cast<const __bf16*>(p.conv_state_in) + ((size_t)m * conv_dim + nn) * KW;
         __bf16* so = static_cast<__bf16*>(p.conv_state_out) + ((size_t)m * conv_dim + nn) * KW;

@@ -53,6 +53,13 @@ __device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, u
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x2 __attribute__((__vector_size__(8)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // 8-element vectors: the per-lane operand slice of one 16x32 MFMA fragment,

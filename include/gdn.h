@@ -160,8 +160,8 @@ int gdn_tkg(const void* q, const void* k, const void* v, const float* b,
  * Stage boundaries are bf16: the projections and the conv output are rounded
  * to bf16; a and b are widened to fp32 for the gate.
  * Constraints: H % 128 == 0; num_v_heads % num_k_heads == 0; head dims
- * 8..128, multiples of 8; 1 <= K_win <= 8; B >= 0; H * conv_dim * 2 and
- * B * H * 2 below 2^31 bytes.
+ * 8..128, multiples of 8; 1 <= K_win <= 8; B >= 0; H * conv_dim * 2,
+ * B * H * 2 and B * conv_dim * K_win * 2 below 2^31 bytes.
  */
 int gdn_block_tkg(const void* hidden, const void* W_in_qkv, const void* W_in_z,
                   const void* W_in_a, const void* W_in_b,
