@@ -143,8 +143,9 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
   const int G = Hv / Hk;
   const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
   const int hh = lid % G;
-  const int c = (lid / G) % NC;
-  const int bhk = lid / (G * NC);
+  const int nseg = p.c_end - p.c_begin;
+  const int c = p.c_begin + (lid / G) % nseg;
+  const int bhk = lid / (G * nseg);
   const int b = bhk / Hk, hk = bhk - b * Hk;
   const int h = hk * G + hh;
   const int bh = b * Hv + h;
@@ -388,8 +389,9 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   const int G = Hv / Hk;
   const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
   const int hh = lid % G;
-  const int c = (lid / G) % NC;
-  const int bhk = lid / (G * NC);
+  const int nseg = p.c_end - p.c_begin;
+  const int c = p.c_begin + (lid / G) % nseg;
+  const int bhk = lid / (G * nseg);
   const int b = bhk / Hk, hk = bhk - b * Hk;
   const int h = hk * G + hh;
   const int bh = b * Hv + h;
@@ -927,6 +929,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   const int mt = tid - kThreads;  // mover thread index (movers only)
   const int S = p.S, Dk = p.Dk, Dv = p.Dv, Hv = p.Hv;
   const int NC = (S + C - 1) / C;
+  const int c_begin = p.c_begin, c_end = p.c_end;  // this launch's chunks
   const int ntiles = (Dv + DVT - 1) / DVT;
   const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
   const int tile = lid % ntiles;
@@ -1018,9 +1021,10 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   Regs rs0, rs1;
 
   // descriptors of chunk c (range 0 past the last chunk: the loads read zero)
+  // (chunks outside [c_begin, c_end) read zero and drop their stores)
   auto rem_bytes = [&](int c, int row_elems) -> uint32_t {
     const int r = S - c * C;
-    return r > 0 ? (uint32_t)r * (uint32_t)row_elems * ES : 0u;
+    return (c >= c_begin && c < c_end && r > 0) ? (uint32_t)r * (uint32_t)row_elems * ES : 0u;
   };
   auto ld_k = [&](Regs& m, int c) {
     const auto r = make_rsrc(kg + (size_t)c * C * Dk, rem_bytes(c, Dk));
@@ -1028,7 +1032,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     for (int i = 0; i < NKQ; ++i) m.K[i] = V8::bload(r, vo_kq[i]);
   };
   auto ld_p = [&](Regs& m, int c) {
-    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < NC ? (uint32_t)(C * C) * ES : 0u);
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < c_end ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) m.Pf[s] = V8::bload(r, vo_pf[s]);
   };
@@ -1038,7 +1042,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     for (int s = 0; s < NQ; ++s) m.Qf[s] = V8::bload(r, vo_qf[s]);
   };
   auto ld_t = [&](Regs& m, int c) {
-    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < NC ? (uint32_t)(C * C) * ES : 0u);
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < c_end ? (uint32_t)(C * C) * ES : 0u);
 #pragma unroll
     for (int i = 0; i < NTP; ++i) m.T[i] = V8::bload(r, vo_tp[i]);
   };
@@ -1046,8 +1050,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     const auto rv = make_rsrc(vg + (size_t)c * C * Dv, rem_bytes(c, Dv));
 #pragma unroll
     for (int i = 0; i < NVI; ++i) m.V[i] = V8::bload(rv, vo_v[i]);
-    const int r = S - c * C;
-    const uint32_t nb = r > 0 ? (uint32_t)r * 4u : 0u;
+    const uint32_t nb = rem_bytes(c, 2);  // fp32 per token
     m.g = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
     m.b = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
   };
@@ -1083,7 +1086,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   // instructions (exact waits): items past the tile and chunks outside
   // [0, NC) are dropped by the range check
   auto flush_out = [&](int c) {
-    const auto ro = make_rsrc(og + (ptrdiff_t)c * C * Dv, c >= 0 ? rem_bytes(c, Dv) : 0u);
+    const auto ro = make_rsrc(og + (ptrdiff_t)c * C * Dv, rem_bytes(c, Dv));
 #pragma unroll
     for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
   };
@@ -1143,22 +1146,22 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     // sequence, so the load-to-use waits of each are counted on its own
     // instruction stream.
     __syncthreads();  // T zeroed, initial state staged
-    ld_k(rs0, 0);
-    ld_vg(rs0, 0);
-    ld_t(rs0, 0);
-    st_k(rs0, 0);
+    ld_k(rs0, c_begin);
+    ld_vg(rs0, c_begin);
+    ld_t(rs0, c_begin);
+    st_k(rs0, c_begin & 1);
     st_vg(rs0);
     st_tp(sT, rs0.T);
-    ld_all(rs0, 0);
-    ld_all(rs1, 1);
+    ld_all(rs0, c_begin);
+    ld_all(rs1, c_begin + 1);
     __syncthreads();  // chunk 0 staged
     // an even number of chunks: the padding chunk of an odd count only moves
     // zeros
-    for (int c = 0; c < NC; c += 2) {
+    for (int c = c_begin; c < c_end; c += 2) {
       mover_chunk(rs0, c);
       mover_chunk(rs1, c + 1);
     }
-    flush_out(((NC + 1) & ~1) - 1);
+    flush_out(c_begin + ((c_end - c_begin + 1) & ~1) - 1);
 #ifdef GDN_CTE_PROFILE
     if (tid == kThreads && p.prof) {
       for (int i = 8; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
@@ -1241,7 +1244,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     __syncthreads();
     PROF_MARK(5)
   };
-  for (int c = 0; c < NC; c += 2) {
+  for (int c = c_begin; c < c_end; c += 2) {
     compute_chunk(c);
     compute_chunk(c + 1);
   }
@@ -1266,18 +1269,19 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   }
 }
 
+template <typename T, int DK>
+hipError_t launch_local(const CteParams& p, hipStream_t stream) {
+  const long grid1 = (long)p.B * p.Hv * (p.c_end - p.c_begin);
+  if (grid1 == 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((cte_local1_kernel<DK>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int DK, int DVT>
-hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
-  const int NC = (p.S + kC - 1) / kC;
-  if (NC > 0) {
-    const long grid1 = (long)p.B * p.Hv * NC;
-    if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((cte_local1_kernel<DK>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
-    else
-      hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+hipError_t launch_state(const CteParams& p, hipStream_t stream) {
   const long grid2 = (long)p.B * p.Hv * ((p.Dv + DVT - 1) / DVT);
 #ifndef GDN_CTE_MOVER_WAVES
   constexpr int MW = 4;
@@ -1290,6 +1294,16 @@ hipError_t launch_pair(const CteParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((cte_state_kernel<T, DK, DVT>), dim3((unsigned)grid2), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T, int DK, int DVT>
+hipError_t launch_pair(const CteParams& p0, hipStream_t stream) {
+  CteParams p = p0;
+  p.c_begin = 0;
+  p.c_end = (p.S + kC - 1) / kC;
+  const hipError_t e = launch_local<T, DK>(p, stream);
+  if (e != hipSuccess) return e;
+  return launch_state<T, DK, DVT>(p, stream);
 }
 
 // number of compute units on the target (MI355X)

@@ -45,6 +45,9 @@ struct CteParams {
   int B, Hk, Hv, S, Dk, Dv;
   int has_initial_state;
   float scale;
+  // chunks [c_begin, c_end) of 64 tokens handled by this launch (the
+  // workspace layout and the token indexing always span the whole sequence)
+  int c_begin, c_end;
   // scratch: per (batch * value head, chunk of 64 tokens) the inverse T and
   // the decayed Q K^T block P, each [64][64] in the compute type
   void* ws;

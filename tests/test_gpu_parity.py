@@ -54,6 +54,8 @@ CTE_CASES = [
     (1, 2, 4, 300, 128, 128, "bf16", True),    # ragged, GQA 1:2, in-place state
     (2, 2, 2, 64, 40, 72, "bf16", False),      # padded Dk, Dv not a tile multiple
     (1, 4, 4, 1000, 64, 128, "bf16", True),    # DK = 64 bf16 path
+    (1, 1, 2, 2373, 64, 64, "bf16", True),     # 38 chunks: four segments of 9/10 chunks, ragged tail
+    (1, 1, 1, 1100, 128, 48, "bf16", False),   # 18 chunks: two segments of 9 (odd counts)
 ]
 
 
@@ -132,6 +134,36 @@ def test_cte_long_batched_workload_and_chaining(gpu_lib):
     _sync()
     assert torch.equal(torch.cat(outs, dim=2), out), "chained outputs differ from the single call"
     assert torch.equal(state, st), "chained final state differs from the single call"
+
+
+def test_cte_inside_graph_capture(gpu_lib):
+    """The segmented prefill (chunk-local work on a second stream) captured in a
+    HIP graph: every replay, with eager work and syncs between replays, equals
+    the eager call bit for bit."""
+    import torch
+    d = inputs.cte_inputs(1, 2, 4, 2048 + 64 * 5 + 17, 128, 128, dtype="bf16", state_std=0.05, seed=91)
+    q, k, v, g, be = (dev(d[n]) for n in ("query", "key", "value", "g_log", "beta"))
+    s0 = dev(d["recurrent_state"])
+    st = s0.clone()
+    out = torch.empty((1, 4, q.shape[2], 128), dtype=torch.bfloat16, device=q.device)
+    gpu_lib.gdn_cte(q, k, v, g, be, d["scale"], recurrent_state=st, out=out)  # eager
+    _sync()
+    ref_out, ref_st = out.clone(), st.clone()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        st.copy_(s0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            gpu_lib.gdn_cte(q, k, v, g, be, d["scale"], recurrent_state=st, out=out)
+    for _ in range(3):
+        out.zero_()
+        st.copy_(s0)
+        _sync()
+        graph.replay()
+        _sync()
+        assert torch.equal(out, ref_out), "graph replay output differs from the eager call"
+        assert torch.equal(st, ref_st), "graph replay state differs from the eager call"
 
 
 def test_cte_is_deterministic(gpu_lib):
