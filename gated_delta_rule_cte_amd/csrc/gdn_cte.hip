@@ -366,7 +366,9 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
   return c;
 }
 
-template <int DK>
+// NG value heads that share a key head (GQA) per wave: the raw K K^T and
+// Q K^T products are the same for all of them; only beta and the decays differ.
+template <int DK, int NG>
 __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
@@ -388,13 +390,13 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   const int NC = (S + C - 1) / C;
   const int G = Hv / Hk;
   const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
-  const int hh = lid % G;
+  const int GN = G / NG;  // value-head groups per key head
+  const int hh0 = (lid % GN) * NG;
   const int nseg = p.c_end - p.c_begin;
-  const int c = p.c_begin + (lid / G) % nseg;
-  const int bhk = lid / (G * nseg);
+  const int c = p.c_begin + (lid / GN) % nseg;
+  const int bhk = lid / (GN * nseg);
   const int b = bhk / Hk, hk = bhk - b * Hk;
-  const int h = hk * G + hh;
-  const int bh = b * Hv + h;
+  const int bh0 = b * Hv + hk * G + hh0;  // first value head of this wave
   const int c0 = c * C;
   const uint32_t rem = (uint32_t)(S - c0);
 
@@ -411,20 +413,18 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       kf[rb][s] = V8::bload(rK, off);
       qf[rb][s] = V8::bload(rQ, off);
     }
-  const float gl = buf_load_f32(make_rsrc(p.g + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
-  const float be = buf_load_f32(make_rsrc(p.beta + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
-  sGam[lane] = wave_inclusive_scan_dpp(gl);
-  sBeta[lane] = be;
-  wave_lds_sync();
-  LPROF(0)
-
-  // A (packed, fp32) and P (registers): lane holds row 16 i + lr, columns 16 j + 4 lg .. +3
-  const float scale = p.scale;
-  f4 pacc[kNTri];
+  float gln[NG], ben[NG];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const float gt = sGam[16 * i + lr], bt = sBeta[16 * i + lr];
-    const int t = 16 * i + lr;
+  for (int n = 0; n < NG; ++n) {
+    gln[n] = buf_load_f32(make_rsrc(p.g + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+    ben[n] = buf_load_f32(make_rsrc(p.beta + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+  }
+
+  // raw products of the lower blocks, transposed: lane holds row 16 i + lr,
+  // columns 16 j + 4 lg .. +3 of K K^T and Q K^T
+  f4 kkr[kNTri], qkr[kNTri];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j <= i; ++j) {
       f4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
@@ -433,6 +433,29 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
         kk = MM::mma(kf[j][s], kf[i][s], kk);
         qk = MM::mma(kf[j][s], qf[i][s], qk);
       }
+      kkr[tri(i, j)] = kk;
+      qkr[tri(i, j)] = qk;
+    }
+  const float scale = p.scale;
+
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+  const int bh = bh0 + n;
+  if (n > 0) wave_lds_sync();  // the previous head's LDS reads are done
+  sGam[lane] = wave_inclusive_scan_dpp(gln[n]);
+  sBeta[lane] = ben[n];
+  wave_lds_sync();
+  LPROF(0)
+
+  // A (packed, fp32) and P (registers)
+  f4 pacc[kNTri];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const float gt = sGam[16 * i + lr], bt = sBeta[16 * i + lr];
+    const int t = 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      const f4 kk = kkr[tri(i, j)], qk = qkr[tri(i, j)];
       const float4 gs = *reinterpret_cast<const float4*>(&sGam[16 * j + 4 * lg]);
       const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
       float a[4];
@@ -533,6 +556,7 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
     *reinterpret_cast<uint4*>(Tg + go) = __builtin_bit_cast(uint4, f);
     *reinterpret_cast<uint4*>(Pg + go) = *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
   }
+  }  // value heads
   LPROF(4)
 #ifdef GDN_CTE_PROFILE_LOCAL
   if (tid == 0 && p.prof)
@@ -1273,9 +1297,12 @@ template <typename T, int DK>
 hipError_t launch_local(const CteParams& p, hipStream_t stream) {
   const long grid1 = (long)p.B * p.Hv * (p.c_end - p.c_begin);
   if (grid1 == 0) return hipSuccess;
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((cte_local1_kernel<DK>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
-  else
+  if constexpr (sizeof(T) == 2) {
+    if ((p.Hv / p.Hk) % 2 == 0)
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 2>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
+    else
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 1>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+  } else
     hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
