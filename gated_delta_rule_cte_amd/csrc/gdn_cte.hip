@@ -908,6 +908,29 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
 //   barrier
 // Only the lower 16x16 blocks of T and P are moved; their upper blocks are
 // zeroed once and never written again.
+// element index of (row t, column k) in a K tile: KSW = XOR-swizzled
+// 16-byte granules (granule k/8 of row t lives at granule (k/8) ^ swz(t)),
+// else a plain row pitch
+__device__ __forceinline__ int k_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1) + 8 * ((t >> 3) & 1); }
+template <bool KSW, int PITCH>
+__device__ __forceinline__ int kidx(int t, int k) {
+  if constexpr (KSW) return t * PITCH + ((((k >> 3) ^ k_swz(t)) << 3) | (k & 7));
+  else return t * PITCH + k;
+}
+// the transposed fragment of lds_tr_frag, read from a K tile in either layout:
+// lane l -> K[r0 + 8 (l / 16) + j][c0 + l % 16], j = 0..7
+template <bool KSW, int PITCH>
+__device__ __forceinline__ Vec8<__bf16> k_tr_frag(const __bf16* m, int r0, int c0, int lane) {
+  const int L = lane & 15, g = lane >> 4;
+  const int r = r0 + 8 * g + (L >> 2), c = c0 + 4 * (L & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(m + kidx<KSW, PITCH>(r, c)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(m + kidx<KSW, PITCH>(r + 4, c)));
+  Vec8<__bf16> v;
+  v.u = make_uint4((uint16_t)a[0] | (uint32_t)(uint16_t)a[1] << 16, (uint16_t)a[2] | (uint32_t)(uint16_t)a[3] << 16,
+                   (uint16_t)b[0] | (uint32_t)(uint16_t)b[1] << 16, (uint16_t)b[2] | (uint32_t)(uint16_t)b[3] << 16);
+  return v;
+}
+
 constexpr int kTriItems = (kNB * (kNB + 1) / 2) * 16 * 2;  // 16-byte items in the lower blocks of a C x C tile
 
 template <int DK, int DVT, int MW>
@@ -935,7 +958,14 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   static_assert(kTriItems % kWave == 0 && NVT % kWave == 0, "T and V items end on a wave boundary");
   static_assert(MW == kWaves, "mover wave mw holds the Q and P rows of row block mw");
 
-  __shared__ __align__(16) T sK[2][C * LDK];
+  // K tile: for DK = 128 unpadded 256-byte rows whose 16-byte granules are
+  // XOR-swizzled by row, so the row-fragment reads (16 rows, one granule), the
+  // transposed reads (rows r..r+3 and r+8..r+11, two granules) and the
+  // row-contiguous stores each touch 16 distinct bank groups; DK = 64 keeps a
+  // padded row.
+  constexpr bool KSW = DK == 128;
+  constexpr int LDKS = KSW ? DK : LDK;
+  __shared__ __align__(16) T sK[2][C * LDKS];
   __shared__ __align__(16) T sT[C * LDC];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
@@ -1002,7 +1032,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   for (int i = 0; i < NKQ; ++i) {
     const int it = mt + kMovers * i, t = it / (DK / 8), c8 = 8 * (it % (DK / 8));
     vo_kq[i] = c8 < Dk ? (uint32_t)(t * Dk + c8) * ES : kOOB;
-    lo_kq[i] = t * LDK + c8;
+    lo_kq[i] = kidx<KSW, LDKS>(t, c8);
   }
 #pragma unroll
   for (int i = 0; i < NTP; ++i) {
@@ -1215,7 +1245,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       GC = sEG[C - 1];
       V8 kf[NQ];
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sKc + (16 * w + lr) * LDK + 32 * s + 8 * lg);
+      for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sKc + kidx<KSW, LDKS>(16 * w + lr, 32 * s + 8 * lg));
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f4 kh = {0.f, 0.f, 0.f, 0.f};
@@ -1259,7 +1289,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       hc[0] *= GC; hc[1] *= GC; hc[2] *= GC; hc[3] *= GC;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        hc = MM::mma(lds_tr_frag(sKc, LDK, 32 * s, 16 * kb, lane),
+        hc = MM::mma(k_tr_frag<KSW, LDKS>(sKc, 32 * s, 16 * kb, lane),
                      V8::load(sUd + (16 * vb + lr) * LDC + 32 * s + 8 * lg), hc);
       hacc[j] = hc;
       store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
