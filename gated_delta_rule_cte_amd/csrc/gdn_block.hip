@@ -35,6 +35,7 @@ constexpr int kBM = 64;     // batch rows per workgroup (one 16-row block per wa
 constexpr int kBN = GDN_BLOCK_BN;  // output columns per workgroup
 constexpr int kBK = 128;    // hidden-dimension step
 constexpr int kRing = 4;    // K tiles in flight per workgroup (register ring)
+static_assert(kRing % 2 == 0, "LDS double buffer index = ring slot parity");
 constexpr int kLD = kBK + 8;   // hidden tile pitch (elements)
 constexpr int kLDW = kBN + 8;  // weight tile pitch: 16-byte rows, 2-way banked transposed reads
 
@@ -188,15 +189,20 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
 #pragma unroll
   for (int u = 0; u < kRing; ++u) load(ring[u], u);
 
+  // LDS tiles are double-buffered (tile kt in buffer kt & 1), so one barrier
+  // per K tile suffices: the buffer being written was last read two tiles
+  // ago, before the barrier every wave has since passed.
   auto ring_pass = [&](int kt0) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int kt = kt0 + u;
+      __bf16* sHk = sH + (u & 1) * kBM * kLD;
+      __bf16* sWk = sW + (u & 1) * kBK * kLDW;
       // stage tile kt: hidden and weight rows as they arrived
 #pragma unroll
       for (int i = 0; i < kHItems; ++i) {
         const int it = tid + kThreads * i, m = it / (kBK / 8), k8 = (it % (kBK / 8)) * 8;
-        ring[u].hd[i].store(sH + m * kLD + k8);
+        ring[u].hd[i].store(sHk + m * kLD + k8);
       }
 #pragma unroll
       for (int i = 0; i < kWItems; ++i) {
@@ -207,20 +213,19 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
           v.u.z |= ring[u].wb[i].u.z;
           v.u.w |= ring[u].wb[i].u.w;
         }
-        v.store(sW + kp[i] * kLDW + n8[i]);
+        v.store(sWk + kp[i] * kLDW + n8[i]);
       }
       load(ring[u], kt + kRing);
       __syncthreads();
       if (kt < nkt) {
 #pragma unroll
         for (int s = 0; s < kBK / 32; ++s) {
-          const Vec8<__bf16> a = Vec8<__bf16>::load(sH + (16 * w + lr) * kLD + 32 * s + 8 * lg);
+          const Vec8<__bf16> a = Vec8<__bf16>::load(sHk + (16 * w + lr) * kLD + 32 * s + 8 * lg);
 #pragma unroll
           for (int nb = 0; nb < kBN / 16; ++nb)
-            acc[nb] = Mfma<__bf16>::mma(a, lds_tr_frag(sW, kLDW, 32 * s, 16 * nb, lane), acc[nb]);
+            acc[nb] = Mfma<__bf16>::mma(a, lds_tr_frag(sWk, kLDW, 32 * s, 16 * nb, lane), acc[nb]);
         }
       }
-      __syncthreads();
     }
   };
   if constexpr (NKT > 0) {
@@ -277,8 +282,8 @@ __device__ __forceinline__ void block_proj_body(const BlockParams& p, __bf16* sH
 
 template <int NKT>
 __global__ __launch_bounds__(kThreads) void block_proj_kernel(const BlockParams p) {
-  __shared__ __align__(16) __bf16 sH[kBM * kLD];
-  __shared__ __align__(16) __bf16 sW[kBK * kLDW];
+  __shared__ __align__(16) __bf16 sH[2 * kBM * kLD];
+  __shared__ __align__(16) __bf16 sW[2 * kBK * kLDW];
   const int conv_dim = 2 * p.Hk * p.Dk + p.Hv * p.Dv;
   const int nt_main = (conv_dim + kBN - 1) / kBN + (p.Hv * p.Dv + kBN - 1) / kBN;
   const int nblk = (int)(gridDim.x * gridDim.y);
