@@ -54,8 +54,10 @@ CTE_CASES = [
     (1, 2, 4, 300, 128, 128, "bf16", True),    # ragged, GQA 1:2, in-place state
     (2, 2, 2, 64, 40, 72, "bf16", False),      # padded Dk, Dv not a tile multiple
     (1, 4, 4, 1000, 64, 128, "bf16", True),    # DK = 64 bf16 path
-    (1, 1, 2, 2373, 64, 64, "bf16", True),     # 38 chunks: four segments of 9/10 chunks, ragged tail
-    (1, 1, 1, 1100, 128, 48, "bf16", False),   # 18 chunks: two segments of 9 (odd counts)
+    (1, 1, 2, 2373, 64, 64, "bf16", True),     # 38 chunks, ragged tail
+    (1, 1, 1, 1100, 128, 48, "bf16", False),   # 18 chunks (odd chunk-pair count), one value head per key head
+    (1, 1, 3, 300, 64, 64, "bf16", True),      # GQA 1:3 (odd group: one value head per chunk-local wave)
+    (2, 2, 4, 333, 64, 64, "bf16", True),      # GQA 1:2 with DK = 64 (value-head pairs per wave)
 ]
 
 
