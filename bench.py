@@ -157,6 +157,58 @@ def record_traffic(d):
     print(json.dumps({op: v["bytes_per_call"] for op, v in ops.items()}))
 
 
+def compare_inverse(gdn, torch, dev):
+    """gdn_cte with the default intra-chunk inverse (blocked substitution) and with
+    the doubling Neumann product, at B=1, Hk=16, Hv=32, D=128, bf16, supplied state,
+    for S from 128 to 16384: the kind of comparison the pages report for their two
+    methods (on other hardware).  Inputs drawn on the device with the S=4096
+    workload's distributions; timing only."""
+    rows = []
+    B, Hk, Hv, D = 1, 16, 32, 128
+    for S in (128, 512, 2048, 4096, 16384):
+        g = torch.Generator(device=dev)
+        g.manual_seed(S)
+        q = torch.randn(B, Hk, S, D, device=dev, generator=g)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = torch.randn(B, Hk, S, D, device=dev, generator=g)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn(B, Hv, S, D, device=dev, generator=g).to(torch.bfloat16)
+        gl = -(0.005 + 0.295 * torch.rand(B, Hv, S, device=dev, generator=g))
+        be = 0.05 + 0.9 * torch.rand(B, Hv, S, device=dev, generator=g)
+        st = 0.05 * torch.randn(B, Hv, D, D, device=dev, generator=g)
+        out = torch.empty(B, Hv, S, D, device=dev, dtype=torch.bfloat16)
+        res = {"S": S}
+        for name, algo in (("default_us", gdn.GDN_CTE_ALGO_DEFAULT), ("neumann_us", gdn.GDN_CTE_ALGO_NEUMANN)):
+            def call():
+                gdn.gdn_cte(q, k, v, gl, be, D ** -0.5, recurrent_state=st, algorithm=algo, out=out)
+            call()
+            torch.cuda.synchronize()
+            stream = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(graph, stream=stream):
+                    for _ in range(8):
+                        call()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(2, int(2e5 // S))
+            with torch.cuda.stream(stream):
+                graph.replay()
+                ev0.record(stream)
+                for _ in range(reps):
+                    graph.replay()
+                ev1.record(stream)
+            ev1.synchronize()
+            res[name] = ev0.elapsed_time(ev1) * 1e3 / (reps * 8)
+        res["neumann_over_default"] = res["neumann_us"] / res["default_us"]
+        rows.append(res)
+        print(json.dumps(res), file=sys.stderr, flush=True)
+        del q, k, v, gl, be, st, out, graph
+        torch.cuda.empty_cache()
+    print(json.dumps({"compare_inverse": rows, "config": {"workload": "gdn_cte bf16 B=1 Hk=16 Hv=32 D=128, "
+                      "supplied fp32 state, S = 128 ... 16384"}, "timing": "graphs of 8 calls, HIP events"}))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +222,8 @@ def parse():
                     help="no timing: N plain calls per entry point and input set (for counter runs)")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 counter CSVs in DIR (no GPU needed)")
+    ap.add_argument("--compare-inverse", action="store_true",
+                    help="time gdn_cte with each intra-chunk inverse method over a range of S (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device-to-device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -204,6 +258,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "calls": 5}))
+        return
+
+    if args.compare_inverse:
+        compare_inverse(gdn, torch, dev)
         return
 
     def up(a):

@@ -142,8 +142,9 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
             void* out, int B, int Hk, int Hv, int S, int Dk, int Dv, int dtype, int algorithm,
             void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype %d is not GDN_F32 or GDN_BF16", dtype);
-  if (algorithm != GDN_CTE_ALGO_DEFAULT)
-    return fail(GDN_ERR_UNSUPPORTED, "algorithm %d is not implemented (only GDN_CTE_ALGO_DEFAULT)", algorithm);
+  if (algorithm != GDN_CTE_ALGO_DEFAULT && algorithm != GDN_CTE_ALGO_NEUMANN)
+    return fail(GDN_ERR_UNSUPPORTED, "algorithm %d is not implemented (GDN_CTE_ALGO_DEFAULT or GDN_CTE_ALGO_NEUMANN)",
+                algorithm);
   if (B < 0 || S < 0) return fail(GDN_ERR_SHAPE, "B=%d and S=%d must be >= 0", B, S);
   if (Hk < 1 || Hv < 1 || Hv % Hk != 0) return fail(GDN_ERR_SHAPE, "Hv=%d must be a positive multiple of Hk=%d", Hv, Hk);
   if (!head_dim_ok(Dk) || !head_dim_ok(Dv))
@@ -178,6 +179,7 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
   p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
   p.has_initial_state = has_initial_state ? 1 : 0;
   p.scale = scale;
+  p.algo = algorithm;
   p.ws = workspace;
   p.prof = nullptr;
   return launched(gdn::launch_cte(p, dtype, static_cast<hipStream_t>(stream)));

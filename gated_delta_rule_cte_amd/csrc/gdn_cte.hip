@@ -38,6 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kC = 64;        // chunk length (one 16-row block per wave)
 constexpr int kNB = kC / 16;  // 16-token blocks per chunk
+constexpr int kAlgoNeumann = 1;  // intra-chunk inverse by the doubling Neumann product
 
 #ifdef GDN_CTE_PROFILE
 constexpr int kProfSlots = 16;
@@ -108,7 +109,7 @@ __device__ __forceinline__ T* ws_chunk(void* ws, int bh, int NC, int c) {
 // One workgroup per (batch * value head, chunk).  LDS: the K and Q tiles are
 // dead once the raw products sit in registers, so the fp32 A matrix reuses the
 // K tile's bytes and the staged P block the Q tile's.
-template <typename T, int DK>
+template <typename T, int DK, int ALGO>
 __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) {
   using V8 = Vec8<T>;
   using MM = Mfma<T>;
@@ -248,57 +249,111 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
   __syncthreads();
   LPROF(2)
 
-  // diagonal 16x16 blocks of T: lane = (block, column), forward substitution
-  if (w == 0) {
-    const int blk = lane >> 4, j = lane & 15;
-    const float* Ab = sA + 16 * blk * LDA + 16 * blk;
-    float tc[16];
+  if constexpr (ALGO == kAlgoNeumann) {
+    // T = (I - A)(I + A^2)(I + A^4) ... (I + A^32), as in the bf16 kernel:
+    // Pw <- Pw Pw, T <- T + T Pw, five times; wave w owns block row w of both
+    // (blocks (w, j), j <= w), in accumulator form, and both are kept in row
+    // form in LDS (Pw in sA, T in sTf) as the operands of the next products.
+    f4 pw[NB], tt[NB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+    for (int j = 0; j < NB; ++j)
+      if (j <= w)
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float row[16];
+        for (int r = 0; r < 4; ++r) {
+          const float a = sA[(16 * w + 4 * lg + r) * LDA + 16 * j + lr];
+          pw[j][r] = -a;
+          tt[j][r] = (j == w && 4 * lg + r == lr) ? 1.f - a : -a;
+        }
+    __syncthreads();
+    auto put = [&](float* dst, const f4* src) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(Ab + i * LDA + 4 * q);
-        row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
-      }
-      float acc = 0.f;
+      for (int j = 0; j < NB; ++j)
+        if (j <= w)
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
-      if (i > j) tc[i] = -acc;
+          for (int r = 0; r < 4; ++r) dst[(16 * w + 4 * lg + r) * LDA + 16 * j + lr] = src[j][r];
+    };
+    put(sA, pw);
+    put(sTf, tt);
+    __syncthreads();
+    // block (w, j) of X Y with X in row form (first operand) and Y in LDS
+    auto prod = [&](const float* X, const float* Y, int j, f4 z) {
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+        if (m >= j && m <= w)
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(X[(16 * w + lr) * LDA + 16 * m + 4 * s4 + lg],
+                                                     Y[(16 * m + 4 * s4 + lg) * LDA + 16 * j + lr], z, 0, 0, 0);
+      return z;
+    };
+#pragma unroll 1
+    for (int step = 1; step < 6; ++step) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (j <= w) pw[j] = prod(sA, sA, j, f4{0.f, 0.f, 0.f, 0.f});
+      __syncthreads();
+      put(sA, pw);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (j <= w) tt[j] = prod(sTf, sA, j, tt[j]);
+      __syncthreads();
+      put(sTf, tt);
+      __syncthreads();
     }
+  } else {
+    // diagonal 16x16 blocks of T: lane = (block, column), forward substitution
+    if (w == 0) {
+      const int blk = lane >> 4, j = lane & 15;
+      const float* Ab = sA + 16 * blk * LDA + 16 * blk;
+      float tc[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
-  }
-  __syncthreads();
-  LPROF(3)
-
-  // off-diagonal blocks, one level (block distance d) at a time
+      for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-  for (int d = 1; d < NB; ++d) {
-    const int bj = w, bi = w + d;
-    if (bi < NB) {
-      f4 z = {0.f, 0.f, 0.f, 0.f};
-      for (int m = bj; m < bi; ++m) {
+      for (int i = 1; i < 16; ++i) {
+        float row[16];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * bi + lr) * LDA + 16 * m + 4 * s + lg],
-                                                   sTf[(16 * m + 4 * s + lg) * LDA + 16 * bj + lr], z, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(Ab + i * LDA + 4 * q);
+          row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
+        if (i > j) tc[i] = -acc;
       }
-      float* Zw = sZ[w];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Zw[(4 * lg + r) * 17 + lr] = z[r];
-      wave_lds_sync();
-      f4 tz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        tz = __builtin_amdgcn_mfma_f32_16x16x4f32(sTf[(16 * bi + lr) * LDA + 16 * bi + 4 * s + lg],
-                                                  Zw[(4 * s + lg) * 17 + lr], tz, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sTf[(16 * bi + 4 * lg + r) * LDA + 16 * bj + lr] = -tz[r];
+      for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
     }
     __syncthreads();
+    LPROF(3)
+
+    // off-diagonal blocks, one level (block distance d) at a time
+#pragma unroll
+    for (int d = 1; d < NB; ++d) {
+      const int bj = w, bi = w + d;
+      if (bi < NB) {
+        f4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int m = bj; m < bi; ++m) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * bi + lr) * LDA + 16 * m + 4 * s + lg],
+                                                     sTf[(16 * m + 4 * s + lg) * LDA + 16 * bj + lr], z, 0, 0, 0);
+        }
+        float* Zw = sZ[w];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Zw[(4 * lg + r) * 17 + lr] = z[r];
+        wave_lds_sync();
+        f4 tz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          tz = __builtin_amdgcn_mfma_f32_16x16x4f32(sTf[(16 * bi + lr) * LDA + 16 * bi + 4 * s + lg],
+                                                    Zw[(4 * s + lg) * 17 + lr], tz, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sTf[(16 * bi + 4 * lg + r) * LDA + 16 * bj + lr] = -tz[r];
+      }
+      __syncthreads();
+    }
   }
 
   LPROF(4)
@@ -368,7 +423,7 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
 
 // NG value heads that share a key head (GQA) per wave: the raw K K^T and
 // Q K^T products are the same for all of them; only beta and the decays differ.
-template <int DK, int NG>
+template <int DK, int NG, int ALGO>
 __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
@@ -472,59 +527,119 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   wave_lds_sync();
   LPROF(1)
 
-  // diagonal blocks of T: lane = (block, column), forward substitution
-  {
-    const int blk = lane >> 4, j = lane & 15;
-    const float* Ab = sA + tri(blk, blk) * kBlkF;
-    float tc[16];
+  if constexpr (ALGO == kAlgoNeumann) {
+    // T = (I - A)(I + A^2)(I + A^4) ... (I + A^32): with Pw the running power
+    // (-A)^(2^j), Pw <- Pw Pw and T <- T + T Pw, five times.  Every factor is
+    // lower block-triangular, so block (i, j) of a product sums m = j..i.
+    // Pw and T live in accumulator form (lane: rows 4 lg + r, column lr) and,
+    // as the first operand of the next products, in row form: Pw in sA, T in sTb.
+    f4 pw[kNTri], tb[kNTri];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float row[16];
+      for (int j = 0; j <= i; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(Ab + i * kLB + 4 * q);
-        row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+        for (int r = 0; r < 4; ++r) {
+          const float a = sA[tri(i, j) * kBlkF + (4 * lg + r) * kLB + lr];
+          pw[tri(i, j)][r] = -a;
+          tb[tri(i, j)][r] = (i == j && 4 * lg + r == lr) ? 1.f - a : -a;
+        }
+    wave_lds_sync();
+    auto put = [&](float* dst, const f4* src) {
+#pragma unroll
+      for (int q = 0; q < kNTri; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[q * kBlkF + (4 * lg + r) * kLB + lr] = src[q][r];
+    };
+    put(sA, pw);
+    put(sTb, tb);
+    wave_lds_sync();
+#pragma unroll 1
+    for (int step = 1; step < 6; ++step) {
+      f4 np[kNTri];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) {
+          f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = j; m <= i; ++m)
+            z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), pw[tri(m, j)], z);
+          np[tri(i, j)] = z;
+        }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) {
+          f4 z = tb[tri(i, j)];
+#pragma unroll
+          for (int m = j; m <= i; ++m)
+            z = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), np[tri(m, j)], z);
+          tb[tri(i, j)] = z;
+        }
+#pragma unroll
+      for (int q = 0; q < kNTri; ++q) pw[q] = np[q];
+      wave_lds_sync();
+      put(sA, pw);
+      put(sTb, tb);
+      wave_lds_sync();
+    }
+    LPROF(2)
+  } else {
+    // diagonal blocks of T: lane = (block, column), forward substitution
+    {
+      const int blk = lane >> 4, j = lane & 15;
+      const float* Ab = sA + tri(blk, blk) * kBlkF;
+      float tc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        float row[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(Ab + i * kLB + 4 * q);
+          row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
+        if (i > j) tc[i] = -acc;
       }
-      float acc = 0.f;
+      float* Tb = sTb + tri(blk, blk) * kBlkF;
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
-      if (i > j) tc[i] = -acc;
+      for (int i = 0; i < 16; ++i) Tb[i * kLB + j] = tc[i];
     }
-    float* Tb = sTb + tri(blk, blk) * kBlkF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Tb[i * kLB + j] = tc[i];
-  }
-  wave_lds_sync();
-  LPROF(2)
+    wave_lds_sync();
+    LPROF(2)
 
-  // T blocks in the accumulator layout (lane: rows 4 lg + r, column lr)
-  f4 tb[kNTri];
+    // T blocks in the accumulator layout (lane: rows 4 lg + r, column lr)
+    f4 tb[kNTri];
 #pragma unroll
-  for (int d = 0; d < NB; ++d)
+    for (int d = 0; d < NB; ++d)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tb[tri(d, d)][r] = sTb[tri(d, d) * kBlkF + (4 * lg + r) * kLB + lr];
+      for (int r = 0; r < 4; ++r) tb[tri(d, d)][r] = sTb[tri(d, d) * kBlkF + (4 * lg + r) * kLB + lr];
 #pragma unroll
-  for (int d = 1; d < NB; ++d) {
+    for (int d = 1; d < NB; ++d) {
 #pragma unroll
-    for (int j = 0; j + d < NB; ++j) {
-      const int i = j + d;
-      f4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j + d < NB; ++j) {
+        const int i = j + d;
+        f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = j; m < i; ++m)
-        z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), tb[tri(m, j)], z);
-      const f4 tz = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, i) * kBlkF + lr * kLB + 4 * lg]), z,
-                              f4{0.f, 0.f, 0.f, 0.f});
-      tb[tri(i, j)] = -tz;
+        for (int m = j; m < i; ++m)
+          z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), tb[tri(m, j)], z);
+        const f4 tz = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, i) * kBlkF + lr * kLB + 4 * lg]), z,
+                                f4{0.f, 0.f, 0.f, 0.f});
+        tb[tri(i, j)] = -tz;
+      }
     }
+#pragma unroll
+    for (int d = 1; d < NB; ++d)
+#pragma unroll
+      for (int j = 0; j + d < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sTb[tri(j + d, j) * kBlkF + (4 * lg + r) * kLB + lr] = tb[tri(j + d, j)][r];
   }
-#pragma unroll
-  for (int d = 1; d < NB; ++d)
-#pragma unroll
-    for (int j = 0; j + d < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sTb[tri(j + d, j) * kBlkF + (4 * lg + r) * kLB + lr] = tb[tri(j + d, j)][r];
   // P (bf16) into the A area, which the levels above no longer read
   T* sP = reinterpret_cast<T*>(sA);
   wave_lds_sync();
@@ -1327,13 +1442,22 @@ template <typename T, int DK>
 hipError_t launch_local(const CteParams& p, hipStream_t stream) {
   const long grid1 = (long)p.B * p.Hv * (p.c_end - p.c_begin);
   if (grid1 == 0) return hipSuccess;
+  const bool neu = p.algo == kAlgoNeumann;
   if constexpr (sizeof(T) == 2) {
-    if ((p.Hv / p.Hk) % 2 == 0)
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 2>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
+    if ((p.Hv / p.Hk) % 2 == 0) {
+      if (neu)
+        hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0,
+                           stream, p);
+      else
+        hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
+    } else if (neu)
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 1, kAlgoNeumann>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
     else
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 1>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
-  } else
-    hipLaunchKernelGGL((cte_local_kernel<T, DK>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 1, 0>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+  } else if (neu)
+    hipLaunchKernelGGL((cte_local_kernel<T, DK, kAlgoNeumann>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((cte_local_kernel<T, DK, 0>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -48,6 +48,9 @@ struct CteParams {
   // chunks [c_begin, c_end) of 64 tokens handled by this launch (the
   // workspace layout and the token indexing always span the whole sequence)
   int c_begin, c_end;
+  // intra-chunk inverse: 0 blocked forward substitution, 1 Neumann series
+  // summed by doubling
+  int algo;
   // scratch: per (batch * value head, chunk of 64 tokens) the inverse T and
   // the decayed Q K^T block P, each [64][64] in the compute type
   void* ws;

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_CTE_ALGO_DEFAULT = 0
+GDN_CTE_ALGO_NEUMANN = 1
 STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTYPE",
           -4: "GDN_ERR_ALIGN", -5: "GDN_ERR_ALIAS", -6: "GDN_ERR_WORKSPACE",
           -7: "GDN_ERR_UNSUPPORTED", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_DEVICE"}

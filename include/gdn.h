@@ -51,9 +51,20 @@ enum {
   GDN_ERR_DEVICE = -9       /* the current device is not a gfx950 GPU          */
 };
 
-/* intra-chunk inverse for gdn_cte: the only method here is blocked forward
- * substitution of (I + A), 16x16 diagonal blocks first. */
-enum { GDN_CTE_ALGO_DEFAULT = 0 };
+/* Intra-chunk inverse T = (I + A)^-1 for gdn_cte ("GDN CTE Kernel API
+ * Reference", gdn_cte: parameter algorithm, which names a default method and
+ * a Neumann-series alternative).  A is strictly lower triangular, so both
+ * methods are exact up to rounding:
+ *   GDN_CTE_ALGO_DEFAULT  blocked forward substitution, 16x16 diagonal blocks
+ *                         by scalar substitution, off-diagonal blocks level by
+ *                         level on fp32 MFMA;
+ *   GDN_CTE_ALGO_NEUMANN  the Neumann series summed by doubling,
+ *                         T = (I - A)(I + A^2)(I + A^4) ... (I + A^32) for
+ *                         64-token chunks (A^64 = 0), ten block-triangular
+ *                         fp32 MFMA products per chunk.
+ * Both accept every shape and state form gdn_cte accepts; results agree to
+ * fp32 rounding of T. */
+enum { GDN_CTE_ALGO_DEFAULT = 0, GDN_CTE_ALGO_NEUMANN = 1 };
 
 /* Largest head dimension (Dk, Dv, K, V) any entry point accepts. */
 #define GDN_MAX_HEAD_DIM 128
@@ -79,7 +90,8 @@ enum { GDN_CTE_ALGO_DEFAULT = 0 };
  *   dtype        GDN_BF16 or GDN_F32: the type of query, key, value and out,
  *                and the MFMA operand type.  Accumulation, the decay cumsum,
  *                the triangular solve and the state are fp32 either way.
- *   algorithm    GDN_CTE_ALGO_DEFAULT; anything else -> GDN_ERR_UNSUPPORTED.
+ *   algorithm    GDN_CTE_ALGO_DEFAULT or GDN_CTE_ALGO_NEUMANN (see above);
+ *                anything else -> GDN_ERR_UNSUPPORTED.
  *   workspace    device scratch of gdn_cte_workspace_size() bytes, 256-byte
  *                aligned, disjoint from every other argument (may be NULL when
  *                that size is 0).  It holds, per value head and chunk of 64

@@ -58,7 +58,8 @@ def cte_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), -3),
-    (dict(algorithm=1), -7),
+    (dict(algorithm=2), -7),
+    (dict(algorithm=-1), -7),
     (dict(Hv=3), -2),
     (dict(Hk=0), -2),
     (dict(Dk=130), -2),

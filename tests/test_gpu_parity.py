@@ -20,10 +20,10 @@ def _sync():
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
-def _run_cte(gdn, d, with_state):
+def _run_cte(gdn, d, with_state, algorithm=0):
     st = dev(d["recurrent_state"]).clone() if with_state else None
     out, state = gdn.gdn_cte(dev(d["query"]), dev(d["key"]), dev(d["value"]), dev(d["g_log"]),
-                             dev(d["beta"]), d["scale"], recurrent_state=st)
+                             dev(d["beta"]), d["scale"], recurrent_state=st, algorithm=algorithm)
     _sync()
     return host(out), host(state)
 
@@ -72,6 +72,39 @@ def test_cte_matches_oracle(gpu_lib, case):
     tol = TOL_F32 if dt == "f32" else TOL_BF16
     assert_close(o, ro, tol, 2, "out")
     assert_close(s, rs, tol, 2, "state")
+
+
+NEUMANN_CASES = [CTE_CASES[i] for i in (0, 1, 2, 4, 6, 8, 9, 10)]
+
+
+@pytest.mark.parametrize("case", NEUMANN_CASES, ids=lambda c: "B{}_Hk{}_Hv{}_S{}_Dk{}_Dv{}_{}_{}".format(
+    *c[:7], "state" if c[7] else "zero"))
+def test_cte_neumann_inverse_matches_oracle(gpu_lib, case):
+    """GDN_CTE_ALGO_NEUMANN (the intra-chunk inverse as the doubling Neumann product)
+    against the same oracle and tolerances as the default method."""
+    B, Hk, Hv, S, Dk, Dv, dt, ws = case
+    d = inputs.cte_inputs(B, Hk, Hv, S, Dk, Dv, dtype=dt, g_range=(-0.5, -0.01),
+                          state_std=0.05 if ws else None, seed=1000 + S)
+    o, s = _run_cte(gpu_lib, d, ws, algorithm=gpu_lib.GDN_CTE_ALGO_NEUMANN)
+    ro, rs = _oracle_cte(d, ws)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(o, ro, tol, 2, "out")
+    assert_close(s, rs, tol, 2, "state")
+
+
+def test_cte_neumann_s4096_workload_close_to_default(gpu_lib):
+    """At the S=4096 GQA workload both inverse methods meet the oracle bar, and they
+    agree with each other far inside it (they differ only in T's fp32 rounding)."""
+    d = inputs.workload_inputs("cte_bf16_b1_hk16_hv32_s4096_d128")
+    o0, s0 = _run_cte(gpu_lib, d, True)
+    o1, s1 = _run_cte(gpu_lib, d, True, algorithm=gpu_lib.GDN_CTE_ALGO_NEUMANN)
+    heads = [(0, h) for h in (0, 7, 18, 31)]
+    ref = _oracle_cte(d, True, heads)
+    for (b, h), (ro, rs) in ref.items():
+        assert_close(o1[b:b + 1, h:h + 1], ro, TOL_BF16, 2, f"out head {h}")
+        assert_close(s1[b:b + 1, h:h + 1], rs, TOL_BF16, 2, f"state head {h}")
+    assert_close(o1, o0.astype(np.float64), 2e-3, 2, "out vs default")
+    assert_close(s1, s0.astype(np.float64), 2e-3, 2, "state vs default")
 
 
 def test_cte_empty_sequence(gpu_lib):

@@ -224,6 +224,35 @@ def test_cte_single_chunk_wy_form_via_triangular_solve(impl, S):
     np.testing.assert_allclose(st[0, 0], Hn, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("S", [1, 2, 17, 64])
+def test_neumann_doubling_product_is_the_exact_chunk_inverse(S):
+    """The alternative intra-chunk inverse ("GDN CTE Kernel API Reference", gdn_cte,
+    parameter algorithm: a Neumann series) read as the series summed by doubling,
+    T = (I - A)(I + A^2)(I + A^4) ... with ceil(log2 S) factors: A is strictly lower
+    triangular, so A^S = 0 and the product equals scipy's triangular inverse of
+    (I + A); the WY chunk form with that T then equals the token recurrence."""
+    rng = np.random.default_rng(40 + S)
+    Dk, Dv = 16, 8
+    q, k, v, g, b, s0 = _rand_cte(rng, 1, 1, 1, S, Dk, Dv)
+    K, Vv, gg, bb, H, Q = k[0, 0], v[0, 0], g[0, 0], b[0, 0], s0[0, 0], q[0, 0]
+    gam = np.cumsum(gg)
+    D = np.exp(gam[:, None] - gam[None, :])
+    A = np.tril(bb[:, None] * (K @ K.T) * D, -1)
+    T = np.eye(S) - A
+    P = -A
+    for _ in range(1, max(1, math.ceil(math.log2(S)))):
+        P = P @ P
+        T = T + T @ P
+    Tref = scipy.linalg.solve_triangular(np.eye(S) + A, np.eye(S), lower=True, unit_diagonal=True)
+    np.testing.assert_allclose(T, Tref, rtol=1e-12, atol=1e-14)
+    U = T @ (bb[:, None] * Vv - (bb * np.exp(gam))[:, None] * (K @ H))
+    O = 0.8 * (np.exp(gam)[:, None] * (Q @ H) + np.tril((Q @ K.T) * D) @ U)
+    o, st = gdn_ref.cte(q, k, v, g, b, 0.8, s0)
+    np.testing.assert_allclose(o[0, 0], O, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st[0, 0], np.exp(gam[-1]) * H + (np.exp(gam[-1] - gam)[:, None] * K).T @ U,
+                               rtol=1e-10, atol=1e-12)
+
+
 @pytest.mark.parametrize("impl", CTE_IMPLS)
 def test_cte_state_norm_bound(impl):
     """||I - beta k k^T||_2 <= 1 for unit k and beta in (0,1), so
