@@ -157,6 +157,55 @@ def record_traffic(d):
     print(json.dumps({op: v["bytes_per_call"] for op, v in ops.items()}))
 
 
+def fused_prefill(gdn, torch, dev, inputs):
+    """gdn_cte_fused at the S=4096 prefill shape (B=1, Hk=16, Hv=32, D=128, bf16,
+    supplied state): raw q, k, per-token decode gates, RMSNormGated output; four
+    seeded input sets in rotation, graphs of 16 calls, HIP events."""
+    import numpy as np
+    B, Hk, Hv, S, D = 1, 16, 32, 4096, 128
+
+    def up(a):
+        if a.dtype == "bf16":
+            return torch.from_numpy(a.data.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a.data).to(dev)
+    d = inputs.cte_fused_inputs(B, Hk, Hv, S, D, D, dtype="bf16", state_std=0.05, seed=11)
+    keys = ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "recurrent_state")
+    base = {k: up(d[k]) for k in keys}
+    sets = []
+    for _ in range(NSETS):
+        s = {k: v.clone() for k, v in base.items()}
+        s["out"] = torch.empty((B, Hv, S, D), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+
+    def call(s):
+        gdn.gdn_cte_fused(s["q"], s["k"], s["v"], s["b"], s["a"], s["A_log"], s["dt_bias"], s["z"],
+                          s["norm_weight"], recurrent_state=s["recurrent_state"], out=s["out"])
+    for s in sets:
+        call(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for r in range(OP_REP):
+                call(sets[r % NSETS])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 12
+    with torch.cuda.stream(stream):
+        graph.replay()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (reps * OP_REP)
+    print(json.dumps({"fused_prefill": {"us": us, "tokens_per_s": B * S / (us * 1e-6)},
+                      "config": {"workload": "gdn_cte_fused bf16 B=1 Hk=16 Hv=32 S=4096 D=128, supplied "
+                                 "fp32 state, decode-style gates (A_log = log U(0.02, 0.2))"},
+                      "timing": f"graphs of {OP_REP} calls over {NSETS} input sets, HIP events"}))
+
+
 def compare_inverse(gdn, torch, dev):
     """gdn_cte with the default intra-chunk inverse (blocked substitution) and with
     the doubling Neumann product, at B=1, Hk=16, Hv=32, D=128, bf16, supplied state,
@@ -222,6 +271,8 @@ def parse():
                     help="no timing: N plain calls per entry point and input set (for counter runs)")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 counter CSVs in DIR (no GPU needed)")
+    ap.add_argument("--fused-prefill", action="store_true",
+                    help="time gdn_cte_fused (decode gates and output norm around the prefill) at the S=4096 shape")
     ap.add_argument("--compare-inverse", action="store_true",
                     help="time gdn_cte with each intra-chunk inverse method over a range of S (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -262,6 +313,9 @@ def main():
 
     if args.compare_inverse:
         compare_inverse(gdn, torch, dev)
+        return
+    if args.fused_prefill:
+        fused_prefill(gdn, torch, dev, inputs)
         return
 
     def up(a):

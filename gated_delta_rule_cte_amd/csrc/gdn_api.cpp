@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -183,6 +184,103 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
   p.ws = workspace;
   p.prof = nullptr;
   return launched(gdn::launch_cte(p, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ gdn_cte_fused
+namespace {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+struct FusedLayout {
+  size_t qn, kn, g, beta, cte, total;  // byte offsets and total size
+};
+FusedLayout fused_layout(int B, int Hk, int Hv, int S, int Dk, int dtype) {
+  FusedLayout L{};
+  const size_t nqk = align256((size_t)B * Hk * S * Dk * esize(dtype));
+  const size_t ng = align256((size_t)B * Hv * S * 4);
+  L.qn = 0;
+  L.kn = L.qn + nqk;
+  L.g = L.kn + nqk;
+  L.beta = L.g + ng;
+  L.cte = L.beta + ng;
+  L.total = L.cte + gdn::cte_workspace_bytes(B, Hv, S, dtype);
+  return L;
+}
+}  // namespace
+
+size_t gdn_cte_fused_workspace_size(int B, int Hk, int Hv, int S, int Dk, int Dv, int dtype) {
+  (void)Dv;
+  if (B <= 0 || Hk <= 0 || Hv <= 0 || S <= 0 || Dk <= 0 || (dtype != GDN_F32 && dtype != GDN_BF16)) return 0;
+  return fused_layout(B, Hk, Hv, S, Dk, dtype).total;
+}
+
+int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, const float* a,
+                  const float* A_log, const float* dt_bias, const void* z, const float* norm_weight,
+                  float* recurrent_state, int has_initial_state, void* out, int B, int Hk, int Hv, int S,
+                  int Dk, int Dv, int dtype, int algorithm, float rms_eps, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype %d is not GDN_F32 or GDN_BF16", dtype);
+  if (algorithm != GDN_CTE_ALGO_DEFAULT && algorithm != GDN_CTE_ALGO_NEUMANN)
+    return fail(GDN_ERR_UNSUPPORTED, "algorithm %d is not implemented (GDN_CTE_ALGO_DEFAULT or GDN_CTE_ALGO_NEUMANN)",
+                algorithm);
+  if (B < 0 || S < 0) return fail(GDN_ERR_SHAPE, "B=%d and S=%d must be >= 0", B, S);
+  if (Hk < 1 || Hv < 1 || Hv % Hk != 0) return fail(GDN_ERR_SHAPE, "Hv=%d must be a positive multiple of Hk=%d", Hv, Hk);
+  if (!head_dim_ok(Dk) || !head_dim_ok(Dv))
+    return fail(GDN_ERR_SHAPE, "Dk=%d, Dv=%d must be multiples of 8 in [8, %d]", Dk, Dv, GDN_MAX_HEAD_DIM);
+  if (!(rms_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "rms_eps must be >= 0");
+  if ((long long)B * Hv * ((Dv + 15) / 16) > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "B*Hv too large");
+  const size_t es = esize(dtype);
+  if ((size_t)S * 256 * es >= ((size_t)1 << 31))
+    return fail(GDN_ERR_SHAPE, "S=%d is too long for one call (per-head data must stay below 2 GiB)", S);
+  const size_t nqk = (size_t)B * Hk * S * Dk * es, nv = (size_t)B * Hv * S * Dv * es;
+  const size_t ng = (size_t)B * Hv * S * 4, ns = (size_t)B * Hv * Dk * Dv * 4, nh = (size_t)Hv * 4;
+  const Span sq{"q", q, nqk}, sk{"k", k, nqk}, sv{"v", v, nv}, sb{"b", b, ng}, sa{"a", a, ng},
+      sal{"A_log", A_log, nh}, sdt{"dt_bias", dt_bias, nh}, sz{"z", z, nv},
+      sw{"norm_weight", norm_weight, (size_t)Dv * 4}, st{"recurrent_state", recurrent_state, ns},
+      so{"out", out, nv};
+  if (int r = check_ptrs({sq, sk, sv, sb, sa, sal, sdt, sz, sw, st, so})) return r;
+  if (int r = check_disjoint(so, {sq, sk, sv, sb, sa, sal, sdt, sz, sw, st})) return r;
+  if (int r = check_disjoint(st, {sq, sk, sv, sb, sa, sal, sdt, sz, sw})) return r;
+  if ((size_t)B * Hv == 0) return ok();
+  const FusedLayout L = fused_layout(B, Hk, Hv, S, Dk, dtype);
+  if (S > 0) {
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", L.total);
+    if (workspace_bytes < L.total)
+      return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    const Span ws{"workspace", workspace, L.total};
+    if (int r = check_disjoint(ws, {sq, sk, sv, sb, sa, sal, sdt, sz, sw, st, so})) return r;
+  }
+  if (int r = check_device()) return r;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  gdn::FusedPre f{};
+  f.q = q; f.k = k;
+  f.qn = S > 0 ? w + L.qn : nullptr;
+  f.kn = S > 0 ? w + L.kn : nullptr;
+  f.b = b; f.a = a; f.A_log = A_log; f.dt_bias = dt_bias;
+  f.g = S > 0 ? reinterpret_cast<float*>(w + L.g) : nullptr;
+  f.beta = S > 0 ? reinterpret_cast<float*>(w + L.beta) : nullptr;
+  f.rows_qk = (long)B * Hk * S;
+  f.tokens_v = (long)B * Hv * S;
+  f.S = S; f.Hv = Hv; f.Dk = Dk;
+  hipError_t e = gdn::launch_fused_pre(f, dtype, hs);
+  if (e != hipSuccess) return launched(e);
+  gdn::CteParams p;
+  p.q = f.qn; p.k = f.kn; p.v = v; p.g = f.g; p.beta = f.beta;
+  p.state = recurrent_state; p.out = out;
+  p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
+  p.has_initial_state = has_initial_state ? 1 : 0;
+  p.scale = 1.0f / sqrtf((float)Dk);
+  p.algo = algorithm;
+  p.ws = S > 0 ? w + L.cte : nullptr;
+  p.prof = nullptr;
+  e = gdn::launch_cte(p, dtype, hs);
+  if (e != hipSuccess) return launched(e);
+  gdn::FusedPost post{};
+  post.out = out; post.z = z; post.norm_weight = norm_weight;
+  post.rows = (long)B * Hv * S;
+  post.Dv = Dv;
+  post.rms_eps = rms_eps;
+  return launched(gdn::launch_fused_post(post, dtype, hs));
 }
 
 // ------------------------------------------------------------------ gdn_tkg

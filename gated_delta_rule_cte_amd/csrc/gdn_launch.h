@@ -61,6 +61,33 @@ struct CteParams {
 size_t cte_workspace_bytes(int B, int Hv, int S, int dtype);
 hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream);
 
+// ------------------------------------- prefill with the decode gates and norm
+struct FusedPre {
+  const void* q;              // raw [B, Hk, S, Dk], compute type
+  const void* k;
+  void* qn;                   // unit rows out, same layout and type
+  void* kn;
+  const float* b;             // [B, Hv, S]
+  const float* a;
+  const float* A_log;         // [Hv]
+  const float* dt_bias;
+  float* g;                   // [B, Hv, S] out
+  float* beta;
+  long rows_qk;               // B * Hk * S
+  long tokens_v;              // B * Hv * S
+  int S, Hv, Dk;
+};
+struct FusedPost {
+  void* out;                  // [B, Hv, S, Dv] compute type, normalised in place
+  const void* z;              // same layout
+  const float* norm_weight;   // [Dv]
+  long rows;                  // B * Hv * S
+  int Dv;
+  float rms_eps;
+};
+hipError_t launch_fused_pre(const FusedPre& f, int dtype, hipStream_t stream);
+hipError_t launch_fused_post(const FusedPost& f, int dtype, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode layer
 struct BlockParams {
   const void* hidden;      // [B, H] bf16

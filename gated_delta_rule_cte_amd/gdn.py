@@ -25,7 +25,8 @@ STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTY
           -7: "GDN_ERR_UNSUPPORTED", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_DEVICE"}
 
 #: every symbol include/gdn.h declares
-EXPORTS = ("gdn_cte", "gdn_cte_workspace_size", "gdn_tkg", "gdn_block_tkg",
+EXPORTS = ("gdn_cte", "gdn_cte_workspace_size", "gdn_cte_fused", "gdn_cte_fused_workspace_size",
+           "gdn_tkg", "gdn_block_tkg",
            "gdn_block_tkg_workspace_size", "gdn_status_string", "gdn_last_error",
            "gdn_version")
 
@@ -51,6 +52,10 @@ def load(path: str = LIB_PATH):
     lib.gdn_cte.restype = I
     lib.gdn_cte_workspace_size.argtypes = [I] * 7
     lib.gdn_cte_workspace_size.restype = Z
+    lib.gdn_cte_fused.argtypes = [P] * 10 + [I, P] + [I] * 8 + [F, P, Z, P]
+    lib.gdn_cte_fused.restype = I
+    lib.gdn_cte_fused_workspace_size.argtypes = [I] * 7
+    lib.gdn_cte_fused_workspace_size.restype = Z
     lib.gdn_tkg.argtypes = [P] * 12 + [I, I, I, I, I, F, P]
     lib.gdn_tkg.restype = I
     lib.gdn_block_tkg.argtypes = [P] * 14 + [I] * 7 + [F, P, Z, P]
@@ -139,6 +144,47 @@ def gdn_cte(query, key, value, g_log, beta, scale=1.0, recurrent_state=None,
                        float(scale), _ptr(state), int(has_init), _ptr(out),
                        B, Hk, Hv, S, Dk, Dv, dt, int(algorithm), _ptr(ws), ws_bytes,
                        _stream(dev)))
+    return out, state
+
+
+def gdn_cte_fused(q, k, v, b, a, A_log, dt_bias, z, norm_weight, recurrent_state=None,
+                  algorithm=GDN_CTE_ALGO_DEFAULT, rms_eps=1e-6, out=None):
+    """Chunked prefill with the decode step's gates and output norm: RAW q, k
+    [B,Hk,S,Dk]; v, z [B,Hv,S,Dv]; b, a [B,Hv,S] fp32; A_log, dt_bias [Hv];
+    norm_weight [Dv].  Returns (out [B,Hv,S,Dv] = RMSNormGated(o, z), state
+    [B,Hv,Dk,Dv] fp32); a given ``recurrent_state`` is the initial state and is
+    updated in place."""
+    import torch
+    lib = load()
+    B, Hk, S, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[3]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (B, Hk, S, Dk))
+    _req(v, "v", q.dtype, (B, Hv, S, Dv))
+    _req(z, "z", q.dtype, (B, Hv, S, Dv))
+    _req(b, "b", torch.float32, (B, Hv, S))
+    _req(a, "a", torch.float32, (B, Hv, S))
+    _req(A_log, "A_log", torch.float32, (Hv,))
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,))
+    _req(norm_weight, "norm_weight", torch.float32, (Dv,))
+    dev = q.device
+    has_init = recurrent_state is not None
+    if has_init:
+        _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
+        state = recurrent_state
+    else:
+        state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, Hv, S, Dv), dtype=q.dtype, device=dev)
+    else:
+        _req(out, "out", q.dtype, (B, Hv, S, Dv))
+    dt = _dtype_code(q)
+    ws_bytes = lib.gdn_cte_fused_workspace_size(B, Hk, Hv, S, Dk, Dv, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    _check(lib.gdn_cte_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias),
+                             _ptr(z), _ptr(norm_weight), _ptr(state), int(has_init), _ptr(out),
+                             B, Hk, Hv, S, Dk, Dv, dt, int(algorithm), float(rms_eps), _ptr(ws), ws_bytes,
+                             _stream(dev)))
     return out, state
 
 

@@ -105,6 +105,30 @@ def cte_inputs(B, Hk, Hv, S, Dk, Dv, dtype="bf16", g_range=(-0.3, -0.005),
     return out
 
 
+def cte_fused_inputs(B, Hk, Hv, S, Dk, Dv, dtype="bf16", A_range=(0.02, 0.2), state_std=None, seed=0):
+    """Inputs of the prefill with the decode step's gates and norm: raw q, k, v,
+    z ~ N(0,1); b, a ~ N(0,1) fp32 per token of every value head;
+    A_log = log U(A_range), dt_bias ~ U(-1,1) per value head (A_range keeps the
+    per-token decay g = -exp(A_log) softplus(a + dt_bias) near the prefill
+    workloads' U(-0.3, -0.005)); norm_weight = 1 + 0.1 N(0,1); optional state
+    ~ state_std*N(0,1)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hk, S, Dk), dtype=np.float32)
+    k = rng.standard_normal((B, Hk, S, Dk), dtype=np.float32)
+    v = rng.standard_normal((B, Hv, S, Dv), dtype=np.float32)
+    z = rng.standard_normal((B, Hv, S, Dv), dtype=np.float32)
+    b = rng.standard_normal((B, Hv, S))
+    a = rng.standard_normal((B, Hv, S))
+    A_log = np.log(rng.uniform(A_range[0], A_range[1], size=Hv))
+    dt_bias = rng.uniform(-1.0, 1.0, size=Hv)
+    norm_weight = 1.0 + 0.1 * rng.standard_normal(Dv)
+    out = dict(q=cast(q, dtype), k=cast(k, dtype), v=cast(v, dtype), z=cast(z, dtype),
+               b=f32(b), a=f32(a), A_log=f32(A_log), dt_bias=f32(dt_bias), norm_weight=f32(norm_weight))
+    if state_std is not None:
+        out["recurrent_state"] = f32(state_std * rng.standard_normal((B, Hv, Dk, Dv)))
+    return out
+
+
 def _head_params(rng, Hv, V):
     A_log = np.log(rng.uniform(1.0, 16.0, size=Hv))
     dt_bias = rng.uniform(-1.0, 1.0, size=Hv)

@@ -116,6 +116,44 @@ size_t gdn_cte_workspace_size(int B, int Hk, int Hv, int S, int Dk, int Dv,
                               int dtype);
 
 /*
+ * gdn_cte_fused - chunked prefill with the decode step's gates and output norm.
+ * The steps either side of gdn_cte: "GDN CTE Kernel API Reference", gdn_cte
+ * (Notes: q, k must arrive unit-length; return: the output is un-normalised,
+ * with no fused epilogue) and "GDN TKG Kernel API Reference", gdn_tkg (summary:
+ * l2norm(q, k), beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias), the
+ * 1/sqrt(K) query scale, RMSNormGated(out, z)).
+ *
+ *   q, k         [B, Hk, S, Dk] element type `dtype`, RAW (not normalised).
+ *   v, z         [B, Hv, S, Dv] element type `dtype`.
+ *   b, a         [B, Hv, S] fp32 raw beta input (pre-sigmoid) and gate input
+ *                (pre-softplus), per token of every value head.
+ *   A_log, dt_bias [Hv] fp32, indexed by value head.
+ *   norm_weight  [Dv] fp32 RMSNormGated weight.
+ *   recurrent_state, has_initial_state, algorithm: as for gdn_cte.
+ *   out          [B, Hv, S, Dv] element type `dtype`: RMSNormGated(o, z) with
+ *                o the un-normalised prefill output rounded to `dtype`.  Must
+ *                not overlap any input, recurrent_state or the workspace.
+ *   rms_eps      RMSNormGated epsilon (>= 0; the page gives none; 1e-6 typical).
+ *   workspace    gdn_cte_fused_workspace_size() bytes, 256-byte aligned and
+ *                disjoint from every other argument: the normalised q, k, the
+ *                per-token g and beta, and gdn_cte's own workspace.
+ * Computes q^ = l2norm(q), k^ = l2norm(k) (epsilon 1e-6 inside the square
+ * root, rounded to `dtype`), beta = sigmoid(b), g = -exp(A_log[h])
+ * softplus(a + dt_bias[h]), then gdn_cte(q^, k^, v, g, beta, scale = Dk^-1/2),
+ * then out = norm_weight * o / sqrt(mean_Dv(o^2) + rms_eps) * silu(z).
+ * Constraints: those of gdn_cte.  Errors as for gdn_cte.
+ */
+int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b,
+                  const float* a, const float* A_log, const float* dt_bias,
+                  const void* z, const float* norm_weight, float* recurrent_state,
+                  int has_initial_state, void* out, int B, int Hk, int Hv, int S,
+                  int Dk, int Dv, int dtype, int algorithm, float rms_eps,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+size_t gdn_cte_fused_workspace_size(int B, int Hk, int Hv, int S, int Dk,
+                                    int Dv, int dtype);
+
+/*
  * gdn_tkg - fused single-token decode step.
  * "GDN TKG Kernel API Reference", gdn_tkg: summary, parameters, returns,
  * Notes, Dimensions.

@@ -29,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["bf16_round", "l2norm", "sigmoid", "softplus", "silu",
-           "rms_norm_gated", "cte", "tkg", "conv1d_decode", "in_proj",
+           "rms_norm_gated", "cte", "cte_fused", "tkg", "conv1d_decode", "in_proj",
            "block_tkg", "L2_EPS", "RMS_EPS"]
 
 #: epsilon inside the l2 norm: x / sqrt(sum(x^2) + L2_EPS).  The TKG page names
@@ -140,6 +140,33 @@ def cte(query, key, value, g_log, beta, scale=1.0, initial_state=None):
 # --------------------------------------------------------------------------
 # decode step (GDN TKG Kernel API Reference, gdn_tkg)
 # --------------------------------------------------------------------------
+def cte_fused(q, k, v, b, a, A_log, dt_bias, z, norm_weight, initial_state=None, rms_eps=RMS_EPS):
+    """gdn_cte with the decode step's gates before it and its output norm after
+    it: the steps either side of the prefill ("GDN CTE Kernel API Reference",
+    gdn_cte Notes: unit-length q, k; return: un-normalised output) in the form
+    the "GDN TKG Kernel API Reference" summary gives them.
+
+    q, k: [B, Hk, S, Dk] raw; v, z: [B, Hv, S, Dv]; b, a: [B, Hv, S];
+    A_log, dt_bias: [Hv] (value head h); norm_weight: [Dv].
+    q^ = l2norm(q), k^ = l2norm(k), beta = sigmoid(b),
+    g = -exp(A_log[h]) softplus(a + dt_bias[h]);
+    (O, S) = cte(q^, k^, v, g, beta, scale = Dk^-1/2, initial_state);
+    y = RMSNormGated(O, z) per token over Dv.
+
+    Returns (y [B, Hv, S, Dv] in float64, not rounded; S [B, Hv, Dk, Dv]).
+    Reading: the scale is applied after the norm, as in the decode step; every
+    intermediate is exact here (the device rounds q^, k^ and O to its type).
+    """
+    v = np.asarray(v, np.float64)
+    Dk = np.asarray(q).shape[-1]
+    q_unit, k_unit = l2norm(q), l2norm(k)
+    beta_t = sigmoid(b)
+    rate = np.exp(np.asarray(A_log, np.float64))[None, :, None]
+    g = -rate * softplus(np.asarray(a, np.float64) + np.asarray(dt_bias, np.float64)[None, :, None])
+    O, S = cte(q_unit, k_unit, v, g, beta_t, 1.0 / np.sqrt(Dk), initial_state)
+    return rms_norm_gated(O, z, norm_weight, rms_eps), S
+
+
 def tkg(q, k, v, b, a, A_log, dt_bias, z, norm_weight, state_in, num_v_heads,
         rms_eps=RMS_EPS):
     """One fused decode step for BH = B * num_v_heads independent heads.

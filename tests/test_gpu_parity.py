@@ -107,6 +107,37 @@ def test_cte_neumann_s4096_workload_close_to_default(gpu_lib):
     assert_close(s1, s0.astype(np.float64), 2e-3, 2, "state vs default")
 
 
+FUSED_CASES = [
+    # (B, Hk, Hv, S, Dk, Dv, dtype, with_state)
+    (1, 2, 2, 128, 64, 64, "f32", True),
+    (2, 1, 3, 77, 64, 32, "f32", False),
+    (1, 2, 4, 300, 128, 128, "bf16", True),
+    (1, 1, 1, 1100, 128, 48, "bf16", False),
+    (2, 2, 4, 333, 64, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B{}_Hk{}_Hv{}_S{}_Dk{}_Dv{}_{}_{}".format(
+    *c[:7], "state" if c[7] else "zero"))
+@pytest.mark.parametrize("algorithm", [0, 1])
+def test_cte_fused_matches_oracle(gpu_lib, case, algorithm):
+    """gdn_cte_fused (raw q, k; decode gates; RMSNormGated output) against the
+    oracle's composition of the same steps."""
+    B, Hk, Hv, S, Dk, Dv, dt, ws = case
+    d = inputs.cte_fused_inputs(B, Hk, Hv, S, Dk, Dv, dtype=dt, state_std=0.05 if ws else None, seed=2000 + S)
+    st = dev(d["recurrent_state"]).clone() if ws else None
+    y, state = gpu_lib.gdn_cte_fused(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["b"]), dev(d["a"]),
+                                     dev(d["A_log"]), dev(d["dt_bias"]), dev(d["z"]), dev(d["norm_weight"]),
+                                     recurrent_state=st, algorithm=algorithm)
+    _sync()
+    ry, rs = gdn_ref.cte_fused(d["q"].f64(), d["k"].f64(), d["v"].f64(), d["b"].f64(), d["a"].f64(),
+                               d["A_log"].f64(), d["dt_bias"].f64(), d["z"].f64(), d["norm_weight"].f64(),
+                               d["recurrent_state"].f64() if ws else None)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(host(y), ry, tol, 2, "out")
+    assert_close(host(state), rs, tol, 2, "state")
+
+
 def test_cte_empty_sequence(gpu_lib):
     import torch
     d = inputs.cte_inputs(1, 2, 2, 0, 64, 64, dtype="bf16", state_std=0.05, seed=5)

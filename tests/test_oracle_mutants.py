@@ -33,6 +33,12 @@ MUTANTS = [
     ("k from q block", "k = conv_out[:, key_dim:2 * key_dim]", "k = conv_out[:, :key_dim]"),
     ("window order", "np.asarray(conv_state, np.float64)[:, :, 1:]", "np.asarray(conv_state, np.float64)[:, :, :-1]"),
     ("bf16 ties away", "np.round(np.ldexp(m, 8))", "np.floor(np.ldexp(m, 8) + 0.5)"),
+    ("fused gate head order", "rate = np.exp(np.asarray(A_log, np.float64))[None, :, None]",
+     "rate = np.exp(np.asarray(A_log, np.float64))[::-1][None, :, None]"),
+    ("fused beta not sigmoid", "beta_t = sigmoid(b)", "beta_t = np.asarray(b, np.float64)"),
+    ("fused key not normalised", "q_unit, k_unit = l2norm(q), l2norm(k)", "q_unit, k_unit = l2norm(q), k"),
+    ("fused output rescaled", "return rms_norm_gated(O, z, norm_weight, rms_eps), S",
+     "return rms_norm_gated(O, z, norm_weight, rms_eps) * 1.01, S"),
 ]
 
 CHECKS = [
@@ -53,6 +59,7 @@ CHECKS = [
     (pins.test_conv1d_decode_one_hot_and_correlate, {}),
     (pins.test_conv1d_decode_window_after_k_steps_holds_last_inputs, {}),
     (pins.test_block_wiring_split_and_gqa, {}),
+    (pins.test_cte_fused_equals_iterated_decode_steps, dict(Hk=1, Hv=3)),
 ]
 
 

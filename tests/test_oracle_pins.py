@@ -490,3 +490,26 @@ def test_block_wiring_split_and_gqa():
     np.testing.assert_array_equal(st, s2.reshape(B, Hv, Dk, Dv))
     np.testing.assert_array_equal(cs[:, :, -1], x[:, :conv_dim])
     np.testing.assert_array_equal(cs[:, :, :-1], conv_state[:, :, 1:])
+
+
+@pytest.mark.parametrize("Hk,Hv", [(2, 2), (1, 3)])
+def test_cte_fused_equals_iterated_decode_steps(Hk, Hv):
+    """The prefill with the decode gates and norm equals the decode step applied
+    token by token (a decode step is a one-token prefill after the gate and norm
+    prologue, "GDN TKG Kernel API Reference" summary): same final state, and each
+    token's output equals the decode step's (which is rounded to bf16)."""
+    B, S, K, V = 2, 5, 6, 4
+    d = inputs.cte_fused_inputs(B, Hk, Hv, S, K, V, dtype="f32", A_range=(0.5, 4.0), state_std=0.3, seed=70 + Hv)
+    q, k, v, z = d["q"].f64(), d["k"].f64(), d["v"].f64(), d["z"].f64()
+    b, a = d["b"].f64(), d["a"].f64()
+    A_log, dt_bias, w = d["A_log"].f64(), d["dt_bias"].f64(), d["norm_weight"].f64()
+    s0 = d["recurrent_state"].f64()
+    y, st = gdn_ref.cte_fused(q, k, v, b, a, A_log, dt_bias, z, w, s0)
+    rep = [h // (Hv // Hk) for h in range(Hv)]
+    state = s0.reshape(B * Hv, K, V)
+    for t in range(S):
+        yt, state = gdn_ref.tkg(q[:, rep, t].reshape(B * Hv, K), k[:, rep, t].reshape(B * Hv, K),
+                                v[:, :, t].reshape(B * Hv, V), b[:, :, t].reshape(-1), a[:, :, t].reshape(-1),
+                                A_log, dt_bias, z[:, :, t].reshape(B * Hv, V), w, state, Hv)
+        np.testing.assert_allclose(y[:, :, t].reshape(B * Hv, V), yt, rtol=2.0 ** -8, atol=1e-30)
+    np.testing.assert_allclose(st.reshape(B * Hv, K, V), state, rtol=1e-12, atol=1e-14)
