@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = ["bf16_round", "l2norm", "sigmoid", "softplus", "silu",
            "rms_norm_gated", "cte", "cte_fused", "tkg", "conv1d_decode", "in_proj",
-           "block_tkg", "L2_EPS", "RMS_EPS"]
+           "block_tkg", "conv1d_prefill", "block_cte", "L2_EPS", "RMS_EPS"]
 
 #: epsilon inside the l2 norm: x / sqrt(sum(x^2) + L2_EPS).  The TKG page names
 #: "l2norm(q,k)" without a formula; this is the plain reading.
@@ -270,3 +270,60 @@ def block_tkg(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_state,
                 np.asarray(recurrent_state, np.float64).reshape(B * Hv, Dk, Dv),
                 Hv, rms_eps)
     return y.reshape(B, 1, Hv * Dv), new_window, S1.reshape(B, Hv, Dk, Dv)
+
+
+# --------------------------------------------------------------------------
+# prefill counterpart of the decode layer: in_proj over S tokens, the causal
+# conv1d over the sequence, then the prefill with the decode gates and norm
+# --------------------------------------------------------------------------
+def conv1d_prefill(x, conv_state, conv_weight):
+    """The decode conv1d applied along a sequence ("conv + silu + slide-window
+    state", Block TKG page summary, read for S tokens at once).
+
+    x [B, S, C] (bf16 values), conv_state [B, C, K_win] (oldest first),
+    conv_weight [C, K_win].  Per channel the inputs extend the window:
+    e = [conv_state[..., 0], ..., conv_state[..., K_win-1], x_0, ..., x_{S-1}];
+    token t sees e[t+1 .. t+K_win] (tap K_win-1 on x_t) and the returned window
+    is the last K_win entries of e.  Returns (silu(conv) [B, S, C] in float64,
+    new window [B, C, K_win]).
+    """
+    x = np.asarray(x, np.float64)
+    B, S, C = x.shape
+    st = np.asarray(conv_state, np.float64)
+    Kw = st.shape[2]
+    e = np.concatenate([st, np.transpose(x, (0, 2, 1))], axis=2)       # [B, C, K_win + S]
+    w = np.asarray(conv_weight, np.float64)
+    acc = np.zeros((B, C, S))
+    for j in range(Kw):
+        acc += w[None, :, j:j + 1] * e[:, :, 1 + j:1 + j + S]
+    return np.transpose(silu(acc), (0, 2, 1)), e[:, :, S:S + Kw]
+
+
+def block_cte(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_state,
+              A_log, dt_bias, norm_weight, recurrent_state, num_k_heads,
+              num_v_heads, head_k_dim, head_v_dim, rms_eps=RMS_EPS):
+    """Prefill layer: hidden [B, S, H] -> in_proj (bf16 stage outputs) -> conv1d
+    over the sequence (bf16 output) -> split q|k|v (contiguous blocks) ->
+    cte_fused (per-head q, k; GQA by h // (Hv / Hk)) -> [B, S, value_dim].
+
+    Returns (out [B, S, value_dim] in float64, not rounded; conv_state'
+    [B, conv_dim, K_win]; recurrent_state' [B, Hv, Dk, Dv]).  The same
+    readings as block_tkg; the output is left unrounded.
+    """
+    hidden = np.asarray(hidden, np.float64)
+    B, S, H = hidden.shape
+    Hk, Hv, Dk, Dv = num_k_heads, num_v_heads, head_k_dim, head_v_dim
+    key_dim = Hk * Dk
+    x = hidden.reshape(B * S, H)
+    mixed = in_proj(x, W_in_qkv).reshape(B, S, -1)
+    zz = in_proj(x, W_in_z).reshape(B, S, Hv, Dv)
+    aa = in_proj(x, W_in_a).reshape(B, S, Hv)
+    bb = in_proj(x, W_in_b).reshape(B, S, Hv)
+    conv_out, new_window = conv1d_prefill(mixed, conv_state, conv_weight)
+    conv_out = bf16_round(conv_out)
+    q = conv_out[:, :, :key_dim].reshape(B, S, Hk, Dk).transpose(0, 2, 1, 3)
+    k = conv_out[:, :, key_dim:2 * key_dim].reshape(B, S, Hk, Dk).transpose(0, 2, 1, 3)
+    v = conv_out[:, :, 2 * key_dim:].reshape(B, S, Hv, Dv).transpose(0, 2, 1, 3)
+    y, S1 = cte_fused(q, k, v, bb.transpose(0, 2, 1), aa.transpose(0, 2, 1), A_log, dt_bias,
+                      zz.transpose(0, 2, 1, 3), norm_weight, recurrent_state, rms_eps)
+    return y.transpose(0, 2, 1, 3).reshape(B, S, Hv * Dv), new_window, S1

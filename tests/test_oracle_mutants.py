@@ -33,6 +33,10 @@ MUTANTS = [
     ("k from q block", "k = conv_out[:, key_dim:2 * key_dim]", "k = conv_out[:, :key_dim]"),
     ("window order", "np.asarray(conv_state, np.float64)[:, :, 1:]", "np.asarray(conv_state, np.float64)[:, :, :-1]"),
     ("bf16 ties away", "np.round(np.ldexp(m, 8))", "np.floor(np.ldexp(m, 8) + 0.5)"),
+    ("sequence conv tap offset", "acc += w[None, :, j:j + 1] * e[:, :, 1 + j:1 + j + S]",
+     "acc += w[None, :, j:j + 1] * e[:, :, j:j + S]"),
+    ("sequence conv window end", "e[:, :, S:S + Kw]", "e[:, :, S - 1:S - 1 + Kw]"),
+    ("prefill layer k from q block", "k = conv_out[:, :, key_dim:2 * key_dim]", "k = conv_out[:, :, :key_dim]"),
     ("fused gate head order", "rate = np.exp(np.asarray(A_log, np.float64))[None, :, None]",
      "rate = np.exp(np.asarray(A_log, np.float64))[::-1][None, :, None]"),
     ("fused beta not sigmoid", "beta_t = sigmoid(b)", "beta_t = np.asarray(b, np.float64)"),
@@ -60,6 +64,8 @@ CHECKS = [
     (pins.test_conv1d_decode_window_after_k_steps_holds_last_inputs, {}),
     (pins.test_block_wiring_split_and_gqa, {}),
     (pins.test_cte_fused_equals_iterated_decode_steps, dict(Hk=1, Hv=3)),
+    (pins.test_conv1d_prefill_equals_decode_conv_token_by_token, {}),
+    (pins.test_block_cte_equals_iterated_decode_layer, dict(Hk=1, Hv=2)),
 ]
 
 

@@ -513,3 +513,51 @@ def test_cte_fused_equals_iterated_decode_steps(Hk, Hv):
                                 A_log, dt_bias, z[:, :, t].reshape(B * Hv, V), w, state, Hv)
         np.testing.assert_allclose(y[:, :, t].reshape(B * Hv, V), yt, rtol=2.0 ** -8, atol=1e-30)
     np.testing.assert_allclose(st.reshape(B * Hv, K, V), state, rtol=1e-12, atol=1e-14)
+
+
+def test_conv1d_prefill_equals_decode_conv_token_by_token():
+    """The conv over a sequence is the decode conv slid once per token: same
+    outputs and the same final window, for S shorter and longer than K_win."""
+    rng = np.random.default_rng(80)
+    B, C, Kw = 2, 5, 4
+    w = rng.standard_normal((C, Kw))
+    for S in (1, 3, 9):
+        x = gdn_ref.bf16_round(rng.standard_normal((B, S, C)))
+        st0 = gdn_ref.bf16_round(rng.standard_normal((B, C, Kw)))
+        out, win = gdn_ref.conv1d_prefill(x, st0, w)
+        st = st0
+        for t in range(S):
+            o_t, st = gdn_ref.conv1d_decode(x[:, t], st, w)
+            np.testing.assert_allclose(out[:, t], o_t, rtol=1e-14, atol=1e-15)
+        np.testing.assert_array_equal(win, st)
+
+
+@pytest.mark.parametrize("Hk,Hv", [(2, 2), (1, 2)])
+def test_block_cte_equals_iterated_decode_layer(Hk, Hv):
+    """The prefill layer over S tokens equals the decode layer applied once per
+    token (same weights, conv window and state threaded through): final conv
+    window and state agree, and each token's output equals the decode layer's
+    (rounded to bf16)."""
+    rng = np.random.default_rng(90 + Hv)
+    B, S, Dk, Dv, Kw = 2, 4, 4, 3, 3
+    key_dim, value_dim = Hk * Dk, Hv * Dv
+    conv_dim = 2 * key_dim + value_dim
+    H = 8
+    hidden = gdn_ref.bf16_round(rng.standard_normal((B, S, H)))
+    Wqkv = gdn_ref.bf16_round(0.5 * rng.standard_normal((H, conv_dim)))
+    Wz = gdn_ref.bf16_round(0.5 * rng.standard_normal((H, value_dim)))
+    Wa = gdn_ref.bf16_round(0.5 * rng.standard_normal((H, Hv)))
+    Wb = gdn_ref.bf16_round(0.5 * rng.standard_normal((H, Hv)))
+    conv_w = 0.5 * rng.standard_normal((conv_dim, Kw))
+    cs0 = gdn_ref.bf16_round(rng.standard_normal((B, conv_dim, Kw)))
+    A_log, dt_bias = np.log(rng.uniform(0.5, 4, Hv)), rng.uniform(-1, 1, Hv)
+    w = 1 + 0.1 * rng.standard_normal(Dv)
+    S0 = 0.3 * rng.standard_normal((B, Hv, Dk, Dv))
+    y, cs, st = gdn_ref.block_cte(hidden, Wqkv, Wz, Wa, Wb, conv_w, cs0, A_log, dt_bias, w, S0, Hk, Hv, Dk, Dv)
+    c, s = cs0, S0
+    for t in range(S):
+        yt, c, s = gdn_ref.block_tkg(hidden[:, t:t + 1], Wqkv, Wz, Wa, Wb, conv_w, c, A_log, dt_bias, w, s,
+                                     Hk, Hv, Dk, Dv)
+        np.testing.assert_allclose(y[:, t], yt[:, 0], rtol=2.0 ** -8, atol=1e-30)
+    np.testing.assert_array_equal(cs, c)
+    np.testing.assert_allclose(st, s, rtol=1e-12, atol=1e-14)
