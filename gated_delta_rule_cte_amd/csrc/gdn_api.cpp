@@ -283,6 +283,139 @@ int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, c
   return launched(gdn::launch_fused_post(post, dtype, hs));
 }
 
+// ------------------------------------------------------------ gdn_block_cte
+namespace {
+struct BlockCteLayout {
+  size_t mixed, ztok, q, k, v, zh, a, b, g, beta, o, cte, total;  // byte offsets and total size
+};
+BlockCteLayout block_cte_layout(int B, int S, int Hk, int Hv, int Dk, int Dv) {
+  BlockCteLayout L{};
+  const size_t M = (size_t)B * S, key_dim = (size_t)Hk * Dk, value_dim = (size_t)Hv * Dv;
+  const size_t conv_dim = 2 * key_dim + value_dim, nh = align256(M * Hv * 4);
+  size_t off = 0;
+  L.mixed = off; off += align256(M * conv_dim * 2);
+  L.ztok = off; off += align256(M * value_dim * 2);
+  L.q = off; off += align256(M * key_dim * 2);
+  L.k = off; off += align256(M * key_dim * 2);
+  L.v = off; off += align256(M * value_dim * 2);
+  L.zh = off; off += align256(M * value_dim * 2);
+  L.a = off; off += nh;
+  L.b = off; off += nh;
+  L.g = off; off += nh;
+  L.beta = off; off += nh;
+  L.o = off; off += align256(M * value_dim * 2);
+  L.cte = off;
+  L.total = off + gdn::cte_workspace_bytes(B, Hv, S, GDN_BF16);
+  return L;
+}
+}  // namespace
+
+size_t gdn_block_cte_workspace_size(int B, int S, int H, int num_k_heads, int num_v_heads, int head_k_dim,
+                                    int head_v_dim, int K_win) {
+  (void)H;
+  (void)K_win;
+  if (B <= 0 || S <= 0 || num_k_heads <= 0 || num_v_heads <= 0 || head_k_dim <= 0 || head_v_dim <= 0) return 0;
+  return block_cte_layout(B, S, num_k_heads, num_v_heads, head_k_dim, head_v_dim).total;
+}
+
+int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, const void* W_in_a,
+                  const void* W_in_b, const float* conv_weight, const void* conv_state_in, const float* A_log,
+                  const float* dt_bias, const float* norm_weight, const float* recurrent_state_in, void* out,
+                  void* conv_state_out, float* recurrent_state_out, int B, int S, int H, int num_k_heads,
+                  int num_v_heads, int head_k_dim, int head_v_dim, int K_win, int algorithm, float rms_eps,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const int Hk = num_k_heads, Hv = num_v_heads, Dk = head_k_dim, Dv = head_v_dim;
+  if (algorithm != GDN_CTE_ALGO_DEFAULT && algorithm != GDN_CTE_ALGO_NEUMANN)
+    return fail(GDN_ERR_UNSUPPORTED, "algorithm %d is not implemented (GDN_CTE_ALGO_DEFAULT or GDN_CTE_ALGO_NEUMANN)",
+                algorithm);
+  if (B < 0 || S < 0) return fail(GDN_ERR_SHAPE, "B=%d and S=%d must be >= 0", B, S);
+  if (H < 128 || H % 128 != 0) return fail(GDN_ERR_SHAPE, "H=%d must be a positive multiple of 128", H);
+  if (Hk < 1 || Hv < 1 || Hv % Hk != 0)
+    return fail(GDN_ERR_SHAPE, "num_v_heads=%d must be a positive multiple of num_k_heads=%d", Hv, Hk);
+  if (!head_dim_ok(Dk) || !head_dim_ok(Dv))
+    return fail(GDN_ERR_SHAPE, "head dims %d, %d must be multiples of 8 in [8, %d]", Dk, Dv, GDN_MAX_HEAD_DIM);
+  if (K_win < 1 || K_win > 8) return fail(GDN_ERR_SHAPE, "K_win=%d must be in [1, 8]", K_win);
+  if (!(rms_eps >= 0.f)) return fail(GDN_ERR_SHAPE, "rms_eps must be >= 0");
+  const size_t M = (size_t)B * S, key_dim = (size_t)Hk * Dk, value_dim = (size_t)Hv * Dv;
+  const size_t conv_dim = 2 * key_dim + value_dim;
+  const size_t lim = (size_t)1 << 31;
+  if (M * H * 2 >= lim || (size_t)H * conv_dim * 2 >= lim || M * conv_dim * 2 >= lim || M * value_dim * 2 >= lim ||
+      (size_t)B * conv_dim * K_win * 2 >= lim || (size_t)S * 256 * 2 >= lim)
+    return fail(GDN_ERR_SHAPE, "a buffer reaches 2 GiB (B=%d, S=%d, H=%d)", B, S, H);
+  const size_t ns = (size_t)B * Hv * Dk * Dv * 4, ncs = (size_t)B * conv_dim * K_win * 2;
+  const Span sh{"hidden", hidden, M * H * 2}, swq{"W_in_qkv", W_in_qkv, (size_t)H * conv_dim * 2},
+      swz{"W_in_z", W_in_z, (size_t)H * value_dim * 2}, swa{"W_in_a", W_in_a, (size_t)H * Hv * 2},
+      swb{"W_in_b", W_in_b, (size_t)H * Hv * 2}, scw{"conv_weight", conv_weight, conv_dim * K_win * 4},
+      scs{"conv_state_in", conv_state_in, ncs}, sal{"A_log", A_log, (size_t)Hv * 4},
+      sdt{"dt_bias", dt_bias, (size_t)Hv * 4}, snw{"norm_weight", norm_weight, (size_t)Dv * 4},
+      srs{"recurrent_state_in", recurrent_state_in, ns}, so{"out", out, M * value_dim * 2},
+      sco{"conv_state_out", conv_state_out, ncs}, sro{"recurrent_state_out", recurrent_state_out, ns};
+  if (int r = check_ptrs({sh, swq, swz, swa, swb, scw, scs, sal, sdt, snw, srs, so, sco, sro})) return r;
+  const std::vector<Span> ins{sh, swq, swz, swa, swb, scw, scs, sal, sdt, snw, srs};
+  if (int r = check_disjoint(so, {sh, swq, swz, swa, swb, scw, scs, sal, sdt, snw, srs, sco, sro})) return r;
+  if (int r = check_disjoint(sco, ins, conv_state_in)) return r;
+  if (int r = check_disjoint(sro, ins, recurrent_state_in)) return r;
+  if (int r = check_disjoint(sco, {sro})) return r;
+  if (B == 0) return ok();
+  const BlockCteLayout L = block_cte_layout(B, S, Hk, Hv, Dk, Dv);
+  if (S > 0) {
+    if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes required)", L.total);
+    if (workspace_bytes < L.total)
+      return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, L.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    const Span ws{"workspace", workspace, L.total};
+    if (int r = check_disjoint(ws, {sh, swq, swz, swa, swb, scw, scs, sal, sdt, snw, srs, so, sco, sro})) return r;
+  }
+  if (int r = check_device()) return r;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (recurrent_state_out != recurrent_state_in)
+    e = hipMemcpyAsync(recurrent_state_out, recurrent_state_in, ns, hipMemcpyDeviceToDevice, hs);
+  if (e != hipSuccess) return launched(e);
+  if (S == 0) {
+    if (conv_state_out != conv_state_in)
+      e = hipMemcpyAsync(conv_state_out, conv_state_in, ncs, hipMemcpyDeviceToDevice, hs);
+    return launched(e);
+  }
+  char* w = static_cast<char*>(workspace);
+  gdn::GemmParams gq{hidden, W_in_qkv, w + L.mixed, (int)M, (int)conv_dim, H};
+  if ((e = gdn::launch_gemm_bf16(gq, hs)) != hipSuccess) return launched(e);
+  gdn::GemmParams gz{hidden, W_in_z, w + L.ztok, (int)M, (int)value_dim, H};
+  if ((e = gdn::launch_gemm_bf16(gz, hs)) != hipSuccess) return launched(e);
+  gdn::NarrowParams na{hidden, W_in_a, W_in_b, reinterpret_cast<float*>(w + L.a), reinterpret_cast<float*>(w + L.b),
+                       (int)M, Hv, H, S};
+  if ((e = gdn::launch_proj_narrow(na, hs)) != hipSuccess) return launched(e);
+  gdn::ConvSplitParams cs{};
+  cs.mixed = w + L.mixed; cs.z_tok = w + L.ztok; cs.conv_weight = conv_weight; cs.conv_state = conv_state_in;
+  cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v; cs.z_head = w + L.zh;
+  cs.B = B; cs.S = S; cs.conv_dim = (int)conv_dim; cs.value_dim = (int)value_dim; cs.key_dim = (int)key_dim;
+  cs.Hk = Hk; cs.Hv = Hv; cs.Dk = Dk; cs.Dv = Dv; cs.K_win = K_win;
+  if ((e = gdn::launch_conv_split(cs, hs)) != hipSuccess) return launched(e);
+  gdn::FusedPre f{};
+  f.q = w + L.q; f.k = w + L.k; f.qn = w + L.q; f.kn = w + L.k;
+  f.b = reinterpret_cast<float*>(w + L.b); f.a = reinterpret_cast<float*>(w + L.a);
+  f.A_log = A_log; f.dt_bias = dt_bias;
+  f.g = reinterpret_cast<float*>(w + L.g); f.beta = reinterpret_cast<float*>(w + L.beta);
+  f.rows_qk = (long)B * Hk * S; f.tokens_v = (long)B * Hv * S;
+  f.S = S; f.Hv = Hv; f.Dk = Dk;
+  if ((e = gdn::launch_fused_pre(f, GDN_BF16, hs)) != hipSuccess) return launched(e);
+  gdn::CteParams p;
+  p.q = w + L.q; p.k = w + L.k; p.v = w + L.v; p.g = f.g; p.beta = f.beta;
+  p.state = recurrent_state_out; p.out = w + L.o;
+  p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
+  p.has_initial_state = 1;
+  p.scale = 1.0f / sqrtf((float)Dk);
+  p.algo = algorithm;
+  p.ws = w + L.cte;
+  p.prof = nullptr;
+  if ((e = gdn::launch_cte(p, GDN_BF16, hs)) != hipSuccess) return launched(e);
+  gdn::FusedPost post{};
+  post.out = w + L.o; post.z = w + L.zh; post.norm_weight = norm_weight;
+  post.rows = (long)B * Hv * S; post.Dv = Dv; post.rms_eps = rms_eps;
+  post.out_tok = out; post.S = S; post.Hv = Hv;
+  return launched(gdn::launch_fused_post(post, GDN_BF16, hs));
+}
+
 // ------------------------------------------------------------------ gdn_tkg
 int gdn_tkg(const void* q, const void* k, const void* v, const float* b, const float* a,
             const float* A_log, const float* dt_bias, const void* z, const float* norm_weight,

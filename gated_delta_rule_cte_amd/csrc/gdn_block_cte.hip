@@ -1,0 +1,274 @@
+// Prefill counterpart of the decode layer: in_proj over S tokens, the causal
+// depthwise conv1d over the sequence, then the prefill with the decode gates
+// and output norm.  "GDN Block TKG Kernel API Reference" (summary: in_proj ->
+// conv + silu + slide-window state -> q|k|v split -> GQA -> the GDN step)
+// read for a whole sequence, with "GDN CTE Kernel API Reference" gdn_cte as
+// the recurrence.
+//
+//   gemm_bf16_kernel     [M, H] x [H, N] on bf16 MFMA 16x16x32 (the q|k|v and
+//                        z projections), 128x128 tiles, K step 64 double-
+//                        buffered in LDS, weights read with transposing LDS
+//                        reads, outputs staged through LDS for 16-byte stores;
+//   proj_narrow_kernel   the a and b projections (N = Hv), one wave per token;
+//   conv_split_kernel    conv + silu over the sequence, split into head-major
+//                        q, k, v (and z), rounded to bf16;
+//   conv_window_kernel   the conv window after the last token.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kGBM = 128, kGBN = 128, kGBK = 64;
+constexpr int kGLA = kGBK + 8;  // A tile pitch: 144-byte rows, conflict-free 16-byte fragment reads
+constexpr int kGLB = kGBN + 8;  // B tile pitch: 272-byte rows for the transposed reads
+constexpr int kGLC = kGBN + 8;  // output staging pitch
+constexpr int kGItems = kGBM * kGBK / 8 / kGThreads;  // 16-byte pieces per thread per tile (4)
+static_assert(kGBM * kGBK == kGBK * kGBN, "A and B tiles hold the same number of pieces");
+static_assert(kGBM * kGLC <= 2 * kGBM * kGLA, "output staging fits the A buffers");
+
+__global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(const GemmParams g) {
+  using V8 = Vec8<__bf16>;
+  using MM = Mfma<__bf16>;
+  __shared__ __align__(16) __bf16 sA[2 * kGBM * kGLA];
+  __shared__ __align__(16) __bf16 sB[2 * kGBK * kGLB];
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int M = g.M, N = g.N, K = g.K;
+  const int ntn = (N + kGBN - 1) / kGBN;
+  // neighbouring logical tiles share an M band (the same activation rows)
+  const int lid = xcd_logical_id((int)blockIdx.x, (int)gridDim.x);
+  const int m0 = (lid / ntn) * kGBM, n0 = (lid % ntn) * kGBN;
+  const int wm = 64 * (w >> 1), wn = 64 * (w & 1);
+
+  const auto rA = make_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
+  const auto rB = make_rsrc(g.B, (uint32_t)((size_t)K * N * 2));
+  uint32_t voA[kGItems], voB[kGItems];
+  int loA[kGItems], loB[kGItems];
+#pragma unroll
+  for (int i = 0; i < kGItems; ++i) {
+    const int it = tid + kGThreads * i;
+    const int ar = it / (kGBK / 8), ak = 8 * (it % (kGBK / 8));
+    voA[i] = m0 + ar < M ? (uint32_t)((m0 + ar) * K + ak) * 2u : kOOB;
+    loA[i] = ar * kGLA + ak;
+    const int bk = it / (kGBN / 8), bn = 8 * (it % (kGBN / 8));
+    voB[i] = n0 + bn < N ? (uint32_t)(bk * N + n0 + bn) * 2u : kOOB;
+    loB[i] = bk * kGLB + bn;
+  }
+  V8 ra[kGItems], rb[kGItems];
+  auto load = [&](int kt) {
+    const uint32_t da = (uint32_t)(kt * kGBK) * 2u, db = (uint32_t)(kt * kGBK) * (uint32_t)N * 2u;
+#pragma unroll
+    for (int i = 0; i < kGItems; ++i) {
+      ra[i] = V8::bload(rA, voA[i] == kOOB ? kOOB : voA[i] + da);
+      rb[i] = V8::bload(rB, voB[i] == kOOB ? kOOB : voB[i] + db);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kGItems; ++i) {
+      ra[i].store(sA + buf * kGBM * kGLA + loA[i]);
+      rb[i].store(sB + buf * kGBK * kGLB + loB[i]);
+    }
+  };
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int nkt = K / kGBK;
+  load(0);
+  stage(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) load(kt + 1);
+    const __bf16* a = sA + buf * kGBM * kGLA;
+    const __bf16* bt = sB + buf * kGBK * kGLB;
+#pragma unroll
+    for (int s = 0; s < kGBK / 32; ++s) {
+      V8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = V8::load(a + (wm + 16 * i + lr) * kGLA + 32 * s + 8 * lg);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = lds_tr_frag(bt, kGLB, 32 * s, wn + 16 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = MM::mma(af[i], bf[j], acc[i][j]);
+    }
+    if (kt + 1 < nkt) stage(buf ^ 1);
+    __syncthreads();
+  }
+  // outputs: accumulators -> bf16 tile in LDS -> 16-byte row pieces
+  __bf16* sc = sA;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[(wm + 16 * i + 4 * lg + r) * kGLC + wn + 16 * j + lr] = f2bf(acc[i][j][r]);
+  __syncthreads();
+  const auto rC = make_rsrc(g.C, (uint32_t)((size_t)M * N * 2));
+#pragma unroll
+  for (int i = 0; i < kGBM * kGBN / 8 / kGThreads; ++i) {
+    const int it = tid + kGThreads * i, r = it / (kGBN / 8), c8 = 8 * (it % (kGBN / 8));
+    const uint32_t off = (m0 + r < M && n0 + c8 < N) ? (uint32_t)((m0 + r) * N + n0 + c8) * 2u : kOOB;
+    V8::load(sc + r * kGLC + c8).bstore(rC, off);
+  }
+}
+
+// out[m, n] = bf16(sum_k A[m, k] W[k, n]) widened to fp32, written head-major
+// [B, Hv, S] (m = b S + t, n = head), for the two narrow projections a and b.
+// One wave per token row: lane l takes k = l, l + 64, ...; eight columns per
+// pass, reduced across the wave with lane shuffles.
+__global__ __launch_bounds__(kGThreads) void proj_narrow_kernel(const NarrowParams p) {
+  const int wv = (int)((blockIdx.x * kGThreads + threadIdx.x) / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (wv >= p.M) return;
+  const int b = wv / p.S, t = wv - b * p.S;
+  const __bf16* x = static_cast<const __bf16*>(p.A) + (size_t)wv * p.K;
+#pragma unroll 1
+  for (int which = 0; which < 2; ++which) {
+    const __bf16* W = static_cast<const __bf16*>(which ? p.Wb : p.Wa);
+    float* out = which ? p.out_b : p.out_a;
+#pragma unroll 1
+    for (int n0 = 0; n0 < p.N; n0 += 8) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int k = lane; k < p.K; k += kWave) {
+        const float xv = bf2f(x[k]);
+        const __bf16* wr = W + (size_t)k * p.N + n0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (n0 + j < p.N) acc[j] += xv * bf2f(wr[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = acc[j];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+        acc[j] = v;
+      }
+      if (lane < 8 && n0 + lane < p.N) {
+        float v = acc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+          if (lane == j) v = acc[j];
+        out[((size_t)b * p.N + n0 + lane) * p.S + t] = bf2f(f2bf(v));
+      }
+    }
+  }
+}
+
+// conv + silu over the sequence for one token and 8 channels, then the split:
+// channels [0, key_dim) -> q, [key_dim, 2 key_dim) -> k, the rest of conv_dim
+// -> v (head-major, bf16); groups past conv_dim copy z to head-major.
+__global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitParams p) {
+  const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
+  const int ngrp = (p.conv_dim + p.value_dim) / 8;
+  if (gid >= (long)p.B * p.S * ngrp) return;
+  const int grp = (int)(gid % ngrp);
+  const long tok = gid / ngrp;  // b * S + t
+  const int b = (int)(tok / p.S), t = (int)(tok - (long)b * p.S);
+  const int c = 8 * grp;
+  float y[8];
+  __bf16* dst;
+  if (c < p.conv_dim) {
+    const __bf16* mixed = static_cast<const __bf16*>(p.mixed);
+    const __bf16* st = static_cast<const __bf16*>(p.conv_state) + ((size_t)b * p.conv_dim + c) * p.K_win;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.K_win; ++j) {
+      const int i = t + 1 + j;  // index into [window | tokens]
+      float e[8];
+      if (i < p.K_win) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = bf2f(st[q * p.K_win + i]);
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(mixed + ((size_t)b * p.S + (i - p.K_win)) * p.conv_dim + c);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          e[2 * q] = __uint_as_float(wd[q] << 16);
+          e[2 * q + 1] = __uint_as_float(wd[q] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += p.conv_weight[(size_t)(c + q) * p.K_win + j] * e[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) y[q] = acc[q] * sigmoidf_(acc[q]);
+    if (c < p.key_dim) {
+      const int h = c / p.Dk, d = c - h * p.Dk;
+      dst = static_cast<__bf16*>(p.q) + (((size_t)b * p.Hk + h) * p.S + t) * p.Dk + d;
+    } else if (c < 2 * p.key_dim) {
+      const int cc = c - p.key_dim, h = cc / p.Dk, d = cc - h * p.Dk;
+      dst = static_cast<__bf16*>(p.k) + (((size_t)b * p.Hk + h) * p.S + t) * p.Dk + d;
+    } else {
+      const int cc = c - 2 * p.key_dim, h = cc / p.Dv, d = cc - h * p.Dv;
+      dst = static_cast<__bf16*>(p.v) + (((size_t)b * p.Hv + h) * p.S + t) * p.Dv + d;
+    }
+  } else {
+    const int cc = c - p.conv_dim, h = cc / p.Dv, d = cc - h * p.Dv;
+    const __bf16* zt = static_cast<const __bf16*>(p.z_tok) + tok * p.value_dim + cc;
+    *reinterpret_cast<uint4*>(static_cast<__bf16*>(p.z_head) + (((size_t)b * p.Hv + h) * p.S + t) * p.Dv + d) =
+        *reinterpret_cast<const uint4*>(zt);
+    return;
+  }
+  bf16x8 f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] = f2bf(y[q]);
+  *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, f);
+}
+
+// the window after the last token: the last K_win entries of [window | tokens]
+// (each thread reads its whole row before writing, so it may update in place)
+__global__ __launch_bounds__(kGThreads) void conv_window_kernel(const ConvSplitParams p) {
+  const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
+  if (gid >= (long)p.B * p.conv_dim) return;
+  const int b = (int)(gid / p.conv_dim), c = (int)(gid - (long)b * p.conv_dim);
+  const __bf16* st = static_cast<const __bf16*>(p.conv_state) + gid * p.K_win;
+  const __bf16* mixed = static_cast<const __bf16*>(p.mixed);
+  __bf16 e[8];
+  for (int i = 0; i < p.K_win; ++i) {
+    const int idx = p.S + i;
+    e[i] = idx < p.K_win ? st[idx] : mixed[((size_t)b * p.S + (idx - p.K_win)) * p.conv_dim + c];
+  }
+  __bf16* out = static_cast<__bf16*>(p.conv_state_out) + gid * p.K_win;
+  for (int i = 0; i < p.K_win; ++i) out[i] = e[i];
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t stream) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  const long tiles = (long)((g.M + kGBM - 1) / kGBM) * ((g.N + kGBN - 1) / kGBN);
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(kGThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream) {
+  if (p.M == 0) return hipSuccess;
+  const long waves_per_block = kGThreads / kWave;
+  hipLaunchKernelGGL(proj_narrow_kernel, dim3((unsigned)((p.M + waves_per_block - 1) / waves_per_block)),
+                     dim3(kGThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
+  const long n = (long)p.B * p.S * ((p.conv_dim + p.value_dim) / 8);
+  if (n > 0)
+    hipLaunchKernelGGL(conv_split_kernel, dim3((unsigned)((n + kGThreads - 1) / kGThreads)), dim3(kGThreads), 0,
+                       stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long nw = (long)p.B * p.conv_dim;
+  if (nw > 0)
+    hipLaunchKernelGGL(conv_window_kernel, dim3((unsigned)((nw + kGThreads - 1) / kGThreads)), dim3(kGThreads), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

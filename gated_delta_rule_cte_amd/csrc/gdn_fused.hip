@@ -102,7 +102,12 @@ __global__ __launch_bounds__(kRowThreads) void rms_gate_rows_kernel(const FusedP
   if (valid) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = w[i] * x[i] * rinv * (zz[i] * sigmoidf_(zz[i]));
-    st8(o + 8 * j, x);
+    T* dst = o;
+    if (f.out_tok) {  // row = (b Hv + h) S + t  ->  token-major [B, S, Hv Dv]
+      const long bh = row / f.S, t = row - bh * f.S, b = bh / f.Hv, h = bh - b * f.Hv;
+      dst = static_cast<T*>(f.out_tok) + ((b * f.S + t) * f.Hv + h) * f.Dv;
+    }
+    st8(dst + 8 * j, x);
   }
 }
 

@@ -84,9 +84,44 @@ struct FusedPost {
   long rows;                  // B * Hv * S
   int Dv;
   float rms_eps;
+  // when not NULL the result goes here token-major, [B, S, Hv * Dv], and `out`
+  // is only read
+  void* out_tok;
+  int S, Hv;
 };
 hipError_t launch_fused_pre(const FusedPre& f, int dtype, hipStream_t stream);
 hipError_t launch_fused_post(const FusedPost& f, int dtype, hipStream_t stream);
+
+// ----------------------------------------------- prefill layer (bf16 only)
+struct GemmParams {
+  const void* A;  // [M, K] bf16 row-major
+  const void* B;  // [K, N] bf16 row-major
+  void* C;        // [M, N] bf16 row-major
+  int M, N, K;    // K % 64 == 0
+};
+hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t stream);
+struct NarrowParams {
+  const void* A;             // [M, K] bf16, M = B * S token rows
+  const void* Wa;            // [K, N] bf16
+  const void* Wb;
+  float* out_a;              // [B, N, S] fp32 (bf16-rounded values)
+  float* out_b;
+  int M, N, K, S;
+};
+hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream);
+struct ConvSplitParams {
+  const void* mixed;         // [B * S, conv_dim] bf16 (the q|k|v projection)
+  const void* z_tok;         // [B * S, value_dim] bf16
+  const float* conv_weight;  // [conv_dim, K_win]
+  const void* conv_state;    // [B, conv_dim, K_win] bf16, oldest first
+  void* conv_state_out;      // same shape; may be conv_state
+  void* q;                   // [B, Hk, S, Dk] bf16
+  void* k;
+  void* v;                   // [B, Hv, S, Dv] bf16
+  void* z_head;              // [B, Hv, S, Dv] bf16
+  int B, S, conv_dim, value_dim, key_dim, Hk, Hv, Dk, Dv, K_win;
+};
+hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode layer
 struct BlockParams {

@@ -26,7 +26,7 @@ STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTY
 
 #: every symbol include/gdn.h declares
 EXPORTS = ("gdn_cte", "gdn_cte_workspace_size", "gdn_cte_fused", "gdn_cte_fused_workspace_size",
-           "gdn_tkg", "gdn_block_tkg",
+           "gdn_block_cte", "gdn_block_cte_workspace_size", "gdn_tkg", "gdn_block_tkg",
            "gdn_block_tkg_workspace_size", "gdn_status_string", "gdn_last_error",
            "gdn_version")
 
@@ -56,6 +56,10 @@ def load(path: str = LIB_PATH):
     lib.gdn_cte_fused.restype = I
     lib.gdn_cte_fused_workspace_size.argtypes = [I] * 7
     lib.gdn_cte_fused_workspace_size.restype = Z
+    lib.gdn_block_cte.argtypes = [P] * 14 + [I] * 9 + [F, P, Z, P]
+    lib.gdn_block_cte.restype = I
+    lib.gdn_block_cte_workspace_size.argtypes = [I] * 8
+    lib.gdn_block_cte_workspace_size.restype = Z
     lib.gdn_tkg.argtypes = [P] * 12 + [I, I, I, I, I, F, P]
     lib.gdn_tkg.restype = I
     lib.gdn_block_tkg.argtypes = [P] * 14 + [I] * 7 + [F, P, Z, P]
@@ -186,6 +190,57 @@ def gdn_cte_fused(q, k, v, b, a, A_log, dt_bias, z, norm_weight, recurrent_state
                              B, Hk, Hv, S, Dk, Dv, dt, int(algorithm), float(rms_eps), _ptr(ws), ws_bytes,
                              _stream(dev)))
     return out, state
+
+
+def gdn_block_cte(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_state,
+                  A_log, dt_bias, norm_weight, recurrent_state, algorithm=GDN_CTE_ALGO_DEFAULT,
+                  rms_eps=1e-6, conv_state_out=None, recurrent_state_out=None, out=None):
+    """Prefill layer over S tokens: hidden [B,S,H] bf16 -> (out [B,S,value_dim]
+    bf16, conv_state' [B,conv_dim,K_win] bf16, recurrent_state' [B,Hv,Dk,Dv]
+    fp32).  Functional by default; pass ``conv_state_out=conv_state`` and/or
+    ``recurrent_state_out=recurrent_state`` to update the caches in place.  All
+    dimensions come from the tensor shapes, as for gdn_block_tkg."""
+    import torch
+    lib = load()
+    B, S, H = hidden.shape
+    conv_dim = W_in_qkv.shape[1]
+    value_dim = W_in_z.shape[1]
+    Hv = W_in_a.shape[1]
+    K_win = conv_weight.shape[1]
+    _, _, Dk, Dv = recurrent_state.shape
+    key_dim = (conv_dim - value_dim) // 2
+    Hk = key_dim // Dk
+    bf = torch.bfloat16
+    _req(hidden, "hidden", bf)
+    _req(W_in_qkv, "W_in_qkv", bf, (H, conv_dim))
+    _req(W_in_z, "W_in_z", bf, (H, value_dim))
+    _req(W_in_a, "W_in_a", bf, (H, Hv))
+    _req(W_in_b, "W_in_b", bf, (H, Hv))
+    _req(conv_weight, "conv_weight", torch.float32, (conv_dim, K_win))
+    _req(conv_state, "conv_state", bf, (B, conv_dim, K_win))
+    _req(A_log, "A_log", torch.float32, (Hv,))
+    _req(dt_bias, "dt_bias", torch.float32, (Hv,))
+    _req(norm_weight, "norm_weight", torch.float32, (Dv,))
+    _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
+    if value_dim != Hv * Dv or key_dim * 2 + value_dim != conv_dim or Hk * Dk != key_dim:
+        raise ValueError("inconsistent block shapes")
+    dev = hidden.device
+    if out is None:
+        out = torch.empty((B, S, value_dim), dtype=bf, device=dev)
+    else:
+        _req(out, "out", bf, (B, S, value_dim))
+    if conv_state_out is None:
+        conv_state_out = torch.empty_like(conv_state)
+    if recurrent_state_out is None:
+        recurrent_state_out = torch.empty_like(recurrent_state)
+    ws_bytes = lib.gdn_block_cte_workspace_size(B, S, H, Hk, Hv, Dk, Dv, K_win)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    _check(lib.gdn_block_cte(_ptr(hidden), _ptr(W_in_qkv), _ptr(W_in_z), _ptr(W_in_a), _ptr(W_in_b),
+                             _ptr(conv_weight), _ptr(conv_state), _ptr(A_log), _ptr(dt_bias),
+                             _ptr(norm_weight), _ptr(recurrent_state), _ptr(out), _ptr(conv_state_out),
+                             _ptr(recurrent_state_out), B, S, H, Hk, Hv, Dk, Dv, K_win, int(algorithm),
+                             float(rms_eps), _ptr(ws), ws_bytes, _stream(dev)))
+    return out, conv_state_out, recurrent_state_out
 
 
 def gdn_tkg(q, k, v, b, a, A_log, dt_bias, z, norm_weight, state_in,

@@ -180,6 +180,33 @@ def block_inputs(B, H, Hk, Hv, Dk, Dv, K_win=4, w_std=0.02, conv_w_std=0.5,
                 num_k_heads=Hk, num_v_heads=Hv, head_k_dim=Dk, head_v_dim=Dv)
 
 
+def block_cte_inputs(B, S, H, Hk, Hv, Dk, Dv, K_win=4, w_std=0.02, conv_w_std=0.5,
+                     A_range=(0.02, 0.2), state_std=0.05, seed=5):
+    """Prefill-layer inputs: hidden [B, S, H] ~ N(0,1) bf16 and the decode
+    layer's weights and windows; A_log = log U(A_range) per value head keeps the
+    per-token decay near the prefill workloads' range (as in cte_fused_inputs);
+    dt_bias ~ U(-1,1); norm_weight = 1 + 0.1 N(0,1)."""
+    rng = np.random.default_rng(seed)
+    key_dim, value_dim = Hk * Dk, Hv * Dv
+    conv_dim = 2 * key_dim + value_dim
+    hidden = rng.standard_normal((B, S, H), dtype=np.float32)
+    W_qkv = w_std * rng.standard_normal((H, conv_dim), dtype=np.float32)
+    W_z = w_std * rng.standard_normal((H, value_dim), dtype=np.float32)
+    W_a = w_std * rng.standard_normal((H, Hv), dtype=np.float32)
+    W_b = w_std * rng.standard_normal((H, Hv), dtype=np.float32)
+    conv_w = conv_w_std * rng.standard_normal((conv_dim, K_win), dtype=np.float32)
+    conv_state = rng.standard_normal((B, conv_dim, K_win), dtype=np.float32)
+    A_log = np.log(rng.uniform(A_range[0], A_range[1], size=Hv))
+    dt_bias = rng.uniform(-1.0, 1.0, size=Hv)
+    norm_weight = 1.0 + 0.1 * rng.standard_normal(Dv)
+    state = state_std * rng.standard_normal((B, Hv, Dk, Dv), dtype=np.float32)
+    return dict(hidden=bf16(hidden), W_in_qkv=bf16(W_qkv), W_in_z=bf16(W_z),
+                W_in_a=bf16(W_a), W_in_b=bf16(W_b), conv_weight=f32(conv_w),
+                conv_state=bf16(conv_state), A_log=f32(A_log), dt_bias=f32(dt_bias),
+                norm_weight=f32(norm_weight), recurrent_state=f32(state),
+                num_k_heads=Hk, num_v_heads=Hv, head_k_dim=Dk, head_v_dim=Dv)
+
+
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------

@@ -227,6 +227,49 @@ size_t gdn_block_tkg_workspace_size(int B, int H, int num_k_heads,
                                     int num_v_heads, int head_k_dim,
                                     int head_v_dim, int K_win);
 
+/*
+ * gdn_block_cte - prefill layer: the decode layer's steps over S tokens.
+ * "GDN Block TKG Kernel API Reference", gdn_block_tkg (summary: in_proj ->
+ * depthwise causal conv1d with its window -> q|k|v split and GQA repeat -> the
+ * GDN step) with the conv run along the sequence and gdn_cte_fused as the step
+ * ("GDN CTE Kernel API Reference", gdn_cte).  bf16 only.
+ *
+ *   hidden       [B, S, H] bf16.
+ *   W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, A_log, dt_bias,
+ *   norm_weight  as for gdn_block_tkg.
+ *   conv_state_in [B, conv_dim, K_win] bf16: the window before token 0, oldest
+ *                first.  Per channel the inputs extend it; token t convolves
+ *                the K_win entries ending at its own input (tap K_win-1).
+ *   recurrent_state_in [B, Hv, Dk, Dv] fp32 state before token 0.
+ *   out          [B, S, value_dim] bf16: RMSNormGated(o_t, z_t) per token.
+ *   conv_state_out [B, conv_dim, K_win] bf16: the window after the last token
+ *                (may be exactly conv_state_in).
+ *   recurrent_state_out: the state after the last token (may be exactly
+ *                recurrent_state_in).
+ *   algorithm    intra-chunk inverse, as for gdn_cte.
+ *   workspace    gdn_block_cte_workspace_size() bytes, 256-byte aligned,
+ *                disjoint from every other argument: the projections, the
+ *                head-major conv outputs, gates and the prefill scratch.
+ * Stage boundaries are bf16 as in gdn_block_tkg; q, k are normalised to unit
+ * rows (rounded to bf16) and scaled by Dk^-1/2 inside the prefill.
+ * Constraints: those of gdn_block_tkg, plus S >= 0 and every buffer below
+ * 2^31 bytes (B*S*H*2, B*S*conv_dim*2, H*conv_dim*2, ...).
+ */
+int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z,
+                  const void* W_in_a, const void* W_in_b,
+                  const float* conv_weight, const void* conv_state_in,
+                  const float* A_log, const float* dt_bias,
+                  const float* norm_weight, const float* recurrent_state_in,
+                  void* out, void* conv_state_out, float* recurrent_state_out,
+                  int B, int S, int H, int num_k_heads, int num_v_heads,
+                  int head_k_dim, int head_v_dim, int K_win, int algorithm,
+                  float rms_eps, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+size_t gdn_block_cte_workspace_size(int B, int S, int H, int num_k_heads,
+                                    int num_v_heads, int head_k_dim,
+                                    int head_v_dim, int K_win);
+
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(int status);
 

@@ -138,6 +138,56 @@ def test_cte_fused_matches_oracle(gpu_lib, case, algorithm):
     assert_close(host(state), rs, tol, 2, "state")
 
 
+BLOCK_CTE_CASES = [
+    # (B, S, H, Hk, Hv, Dk, Dv, K_win, in_place, algorithm)
+    (2, 100, 128, 2, 4, 32, 32, 4, False, 0),
+    (1, 300, 256, 1, 2, 64, 64, 3, True, 0),
+    (1, 2, 128, 2, 2, 16, 24, 4, True, 0),      # fewer tokens than the conv window
+    (1, 130, 128, 2, 2, 128, 128, 4, False, 1),  # full head dims, Neumann inverse
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CTE_CASES, ids=lambda c: "B{}_S{}_H{}_Hk{}_Hv{}_Dk{}_Dv{}_W{}_{}_a{}".format(
+    *c[:8], "inplace" if c[8] else "copy", c[9]))
+def test_block_cte_matches_oracle(gpu_lib, case):
+    """gdn_block_cte (in_proj GEMMs, the conv over the sequence, the fused prefill)
+    against the oracle's prefill layer."""
+    import torch
+    B, S, H, Hk, Hv, Dk, Dv, W, in_place, algo = case
+    d = inputs.block_cte_inputs(B, S, H, Hk, Hv, Dk, Dv, K_win=W, seed=3000 + S)
+    cs = dev(d["conv_state"]).clone()
+    rs = dev(d["recurrent_state"]).clone()
+    args = [dev(d[n]) for n in ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight")]
+    out, cs1, rs1 = gpu_lib.gdn_block_cte(*args, cs, dev(d["A_log"]), dev(d["dt_bias"]), dev(d["norm_weight"]), rs,
+                                          algorithm=algo, conv_state_out=cs if in_place else None,
+                                          recurrent_state_out=rs if in_place else None)
+    _sync()
+    ry, rcs, rrs = gdn_ref.block_cte(d["hidden"].f64(), d["W_in_qkv"].f64(), d["W_in_z"].f64(), d["W_in_a"].f64(),
+                                     d["W_in_b"].f64(), d["conv_weight"].f64(), d["conv_state"].f64(),
+                                     d["A_log"].f64(), d["dt_bias"].f64(), d["norm_weight"].f64(),
+                                     d["recurrent_state"].f64(), Hk, Hv, Dk, Dv)
+    assert_close(host(out), ry, TOL_BF16, 1, "out")
+    assert_close(host(rs1), rrs, TOL_BF16, 2, "recurrent state")
+    np.testing.assert_array_equal(host(cs1), rcs)
+    if in_place:
+        assert cs1.data_ptr() == cs.data_ptr() and rs1.data_ptr() == rs.data_ptr()
+
+
+def test_block_cte_one_token_equals_decode_layer(gpu_lib):
+    """One token through the prefill layer and through gdn_block_tkg: the same
+    caches and outputs within the bf16 bar."""
+    d = inputs.block_cte_inputs(3, 1, 256, 2, 4, 64, 64, K_win=4, seed=33)
+    names = ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight")
+    args = [dev(d[n]) for n in names]
+    rest = [dev(d[n]) for n in ("conv_state", "A_log", "dt_bias", "norm_weight", "recurrent_state")]
+    out, cs1, rs1 = gpu_lib.gdn_block_cte(*args, *rest)
+    out2, cs2, rs2 = gpu_lib.gdn_block_tkg(*args, *rest)
+    _sync()
+    np.testing.assert_array_equal(host(cs1), host(cs2))
+    assert_close(host(out), host(out2), TOL_BF16, 1, "out")
+    assert_close(host(rs1), host(rs2), TOL_BF16, 2, "recurrent state")
+
+
 def test_cte_empty_sequence(gpu_lib):
     import torch
     d = inputs.cte_inputs(1, 2, 2, 0, 64, 64, dtype="bf16", state_std=0.05, seed=5)
