@@ -157,6 +157,60 @@ def record_traffic(d):
     print(json.dumps({op: v["bytes_per_call"] for op, v in ops.items()}))
 
 
+def prefill_layer(gdn, torch, dev, inputs):
+    """gdn_block_cte at B=1, S=4096 with the decode layer's model shape (H=2048,
+    Hk=16, Hv=32, D=128, K_win=4): caches updated in place, four seeded input
+    sets in rotation, graphs of 4 calls, HIP events.  Also the in_proj GEMM's
+    share: 2 * B*S * H * (conv_dim + value_dim + 2 Hv) flops on bf16 MFMA."""
+    import numpy as np
+    B, S, H, Hk, Hv, D, Kw = 1, 4096, 2048, 16, 32, 128, 4
+
+    def up(a):
+        if a.dtype == "bf16":
+            return torch.from_numpy(a.data.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a.data).to(dev)
+    d = inputs.block_cte_inputs(B, S, H, Hk, Hv, D, D, K_win=Kw, seed=12)
+    keys = ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight", "conv_state", "A_log",
+            "dt_bias", "norm_weight", "recurrent_state")
+    base = {k: up(d[k]) for k in keys}
+    sets = []
+    for _ in range(NSETS):
+        s = {k: v.clone() for k, v in base.items()}
+        s["out"] = torch.empty((B, S, Hv * D), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+
+    def call(s):
+        gdn.gdn_block_cte(*(s[k] for k in keys), conv_state_out=s["conv_state"],
+                          recurrent_state_out=s["recurrent_state"], out=s["out"])
+    for s in sets:
+        call(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for r in range(NSETS):
+                call(sets[r])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    with torch.cuda.stream(stream):
+        graph.replay()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (reps * NSETS)
+    conv_dim = 2 * Hk * D + Hv * D
+    gemm_flops = 2.0 * B * S * H * (conv_dim + Hv * D + 2 * Hv)
+    print(json.dumps({"prefill_layer": {"us": us, "tokens_per_s": B * S / (us * 1e-6),
+                                        "in_proj_flops": gemm_flops},
+                      "config": {"workload": "gdn_block_cte bf16 B=1 S=4096 H=2048 Hk=16 Hv=32 D=128 K_win=4, "
+                                 "caches in place"},
+                      "timing": f"graphs of {NSETS} calls over {NSETS} input sets, HIP events"}))
+
+
 def fused_prefill(gdn, torch, dev, inputs):
     """gdn_cte_fused at the S=4096 prefill shape (B=1, Hk=16, Hv=32, D=128, bf16,
     supplied state): raw q, k, per-token decode gates, RMSNormGated output; four
@@ -271,6 +325,8 @@ def parse():
                     help="no timing: N plain calls per entry point and input set (for counter runs)")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 counter CSVs in DIR (no GPU needed)")
+    ap.add_argument("--prefill-layer", action="store_true",
+                    help="time gdn_block_cte (in_proj + conv over the sequence + fused prefill) at B=1, S=4096")
     ap.add_argument("--fused-prefill", action="store_true",
                     help="time gdn_cte_fused (decode gates and output norm around the prefill) at the S=4096 shape")
     ap.add_argument("--compare-inverse", action="store_true",
@@ -316,6 +372,9 @@ def main():
         return
     if args.fused_prefill:
         fused_prefill(gdn, torch, dev, inputs)
+        return
+    if args.prefill_layer:
+        prefill_layer(gdn, torch, dev, inputs)
         return
 
     def up(a):

@@ -286,7 +286,7 @@ int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, c
 // ------------------------------------------------------------ gdn_block_cte
 namespace {
 struct BlockCteLayout {
-  size_t mixed, ztok, q, k, v, zh, a, b, g, beta, o, cte, total;  // byte offsets and total size
+  size_t mixed, ztok, abtok, q, k, v, zh, a, b, g, beta, o, cte, total;  // byte offsets and total size
 };
 BlockCteLayout block_cte_layout(int B, int S, int Hk, int Hv, int Dk, int Dv) {
   BlockCteLayout L{};
@@ -295,6 +295,7 @@ BlockCteLayout block_cte_layout(int B, int S, int Hk, int Hv, int Dk, int Dv) {
   size_t off = 0;
   L.mixed = off; off += align256(M * conv_dim * 2);
   L.ztok = off; off += align256(M * value_dim * 2);
+  L.abtok = off; off += align256(2 * M * Hv * 2);
   L.q = off; off += align256(M * key_dim * 2);
   L.k = off; off += align256(M * key_dim * 2);
   L.v = off; off += align256(M * value_dim * 2);
@@ -378,14 +379,29 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
     return launched(e);
   }
   char* w = static_cast<char*>(workspace);
-  gdn::GemmParams gq{hidden, W_in_qkv, w + L.mixed, (int)M, (int)conv_dim, H};
-  if ((e = gdn::launch_gemm_bf16(gq, hs)) != hipSuccess) return launched(e);
-  gdn::GemmParams gz{hidden, W_in_z, w + L.ztok, (int)M, (int)value_dim, H};
-  if ((e = gdn::launch_gemm_bf16(gz, hs)) != hipSuccess) return launched(e);
-  gdn::NarrowParams na{hidden, W_in_a, W_in_b, reinterpret_cast<float*>(w + L.a), reinterpret_cast<float*>(w + L.b),
-                       (int)M, Hv, H, S};
-  if ((e = gdn::launch_proj_narrow(na, hs)) != hipSuccess) return launched(e);
+  // the four projections in one launch; a and b join it when their rows are
+  // whole 16-byte pieces, else they take one wave per token
+  const bool ab_gemm = Hv % 8 == 0;
+  gdn::GemmParams gp{};
+  gp.A = hidden; gp.M = (int)M; gp.K = H;
+  gp.B[0] = W_in_qkv; gp.C[0] = w + L.mixed; gp.N[0] = (int)conv_dim;
+  gp.B[1] = W_in_z; gp.C[1] = w + L.ztok; gp.N[1] = (int)value_dim;
+  gp.nprob = 2;
+  if (ab_gemm) {
+    gp.B[2] = W_in_a; gp.C[2] = w + L.abtok; gp.N[2] = Hv;
+    gp.B[3] = W_in_b; gp.C[3] = w + L.abtok + M * Hv * 2; gp.N[3] = Hv;
+    gp.nprob = 4;
+  }
+  if ((e = gdn::launch_gemm_bf16(gp, hs)) != hipSuccess) return launched(e);
+  if (!ab_gemm) {
+    gdn::NarrowParams na{hidden, W_in_a, W_in_b, reinterpret_cast<float*>(w + L.a),
+                         reinterpret_cast<float*>(w + L.b), (int)M, Hv, H, S};
+    if ((e = gdn::launch_proj_narrow(na, hs)) != hipSuccess) return launched(e);
+  }
   gdn::ConvSplitParams cs{};
+  cs.ab_tok = ab_gemm ? w + L.abtok : nullptr;
+  cs.a_head = reinterpret_cast<float*>(w + L.a);
+  cs.b_head = reinterpret_cast<float*>(w + L.b);
   cs.mixed = w + L.mixed; cs.z_tok = w + L.ztok; cs.conv_weight = conv_weight; cs.conv_state = conv_state_in;
   cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v; cs.z_head = w + L.zh;
   cs.B = B; cs.S = S; cs.conv_dim = (int)conv_dim; cs.value_dim = (int)value_dim; cs.key_dim = (int)key_dim;

@@ -36,15 +36,24 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(const GemmParams g
 
   const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
   const int lr = lane & 15, lg = lane >> 4;
-  const int M = g.M, N = g.N, K = g.K;
+  const int M = g.M, K = g.K;
+  const int ntm = (M + kGBM - 1) / kGBM;
+  // neighbouring logical tiles share an M band (the same activation rows);
+  // the products' tiles follow one another
+  int lid = xcd_logical_id((int)blockIdx.x, (int)gridDim.x);
+  int pi = 0;
+  for (; pi + 1 < g.nprob; ++pi) {
+    const int nt = ntm * ((g.N[pi] + kGBN - 1) / kGBN);
+    if (lid < nt) break;
+    lid -= nt;
+  }
+  const int N = g.N[pi];
   const int ntn = (N + kGBN - 1) / kGBN;
-  // neighbouring logical tiles share an M band (the same activation rows)
-  const int lid = xcd_logical_id((int)blockIdx.x, (int)gridDim.x);
   const int m0 = (lid / ntn) * kGBM, n0 = (lid % ntn) * kGBN;
   const int wm = 64 * (w >> 1), wn = 64 * (w & 1);
 
   const auto rA = make_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
-  const auto rB = make_rsrc(g.B, (uint32_t)((size_t)K * N * 2));
+  const auto rB = make_rsrc(g.B[pi], (uint32_t)((size_t)K * N * 2));
   uint32_t voA[kGItems], voB[kGItems];
   int loA[kGItems], loB[kGItems];
 #pragma unroll
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(const GemmParams g
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[(wm + 16 * i + 4 * lg + r) * kGLC + wn + 16 * j + lr] = f2bf(acc[i][j][r]);
   __syncthreads();
-  const auto rC = make_rsrc(g.C, (uint32_t)((size_t)M * N * 2));
+  const auto rC = make_rsrc(g.C[pi], (uint32_t)((size_t)M * N * 2));
 #pragma unroll
   for (int i = 0; i < kGBM * kGBN / 8 / kGThreads; ++i) {
     const int it = tid + kGThreads * i, r = it / (kGBN / 8), c8 = 8 * (it % (kGBN / 8));
@@ -163,64 +172,122 @@ __global__ __launch_bounds__(kGThreads) void proj_narrow_kernel(const NarrowPara
   }
 }
 
-// conv + silu over the sequence for one token and 8 channels, then the split:
-// channels [0, key_dim) -> q, [key_dim, 2 key_dim) -> k, the rest of conv_dim
-// -> v (head-major, bf16); groups past conv_dim copy z to head-major.
+// conv + silu over the sequence for 8 channels and a block of kConvTok tokens
+// (the window slides in registers, so each input row is read once), then the
+// split: channels [0, key_dim) -> q, [key_dim, 2 key_dim) -> k, the rest of
+// conv_dim -> v, all head-major bf16.  Further groups move z (8 channels) and,
+// when the narrow projections came from the GEMM, a and b (8 heads) from
+// token-major to head-major.
+constexpr int kConvTok = 16;
+
+__device__ __forceinline__ void unpack8(uint4 u, float* e) {
+  const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    e[2 * q] = __uint_as_float(wd[q] << 16);
+    e[2 * q + 1] = __uint_as_float(wd[q] & 0xFFFF0000u);
+  }
+}
+
+template <int KW>
 __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitParams p) {
+  const int gconv = p.conv_dim / 8, gz = p.value_dim / 8, gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
+  const int ngrp = gconv + gz + gab;
+  const int ntb = (p.S + kConvTok - 1) / kConvTok;
   const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
-  const int ngrp = (p.conv_dim + p.value_dim) / 8;
-  if (gid >= (long)p.B * p.S * ngrp) return;
+  if (gid >= (long)p.B * ntb * ngrp) return;
   const int grp = (int)(gid % ngrp);
-  const long tok = gid / ngrp;  // b * S + t
-  const int b = (int)(tok / p.S), t = (int)(tok - (long)b * p.S);
-  const int c = 8 * grp;
-  float y[8];
-  __bf16* dst;
-  if (c < p.conv_dim) {
-    const __bf16* mixed = static_cast<const __bf16*>(p.mixed);
+  const long btb = gid / ngrp;
+  const int b = (int)(btb / ntb), t0 = (int)(btb - (long)b * ntb) * kConvTok;
+  const int t1 = min(t0 + kConvTok, p.S);
+  if (grp < gconv) {
+    const int c = 8 * grp;
+    const __bf16* mixed = static_cast<const __bf16*>(p.mixed) + (size_t)b * p.S * p.conv_dim + c;
     const __bf16* st = static_cast<const __bf16*>(p.conv_state) + ((size_t)b * p.conv_dim + c) * p.K_win;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.K_win; ++j) {
-      const int i = t + 1 + j;  // index into [window | tokens]
+    constexpr int Kw = KW;
+    // taps and the window (entries of [state | tokens]); token t uses entries t+1 .. t+Kw
+    float wt[8][KW], win[8][KW];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        wt[q][j] = p.conv_weight[(size_t)(c + q) * Kw + j];
+        win[q][j] = 0.f;
+      }
+    // entries t0+1 .. t0+Kw-1 into slots 0 .. Kw-2
+#pragma unroll
+    for (int j = 0; j < KW - 1; ++j) {
+      const int i = t0 + 1 + j;
       float e[8];
-      if (i < p.K_win) {
+      if (i < Kw) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = bf2f(st[q * p.K_win + i]);
+        for (int q = 0; q < 8; ++q) e[q] = bf2f(st[q * Kw + i]);
       } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(mixed + ((size_t)b * p.S + (i - p.K_win)) * p.conv_dim + c);
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          e[2 * q] = __uint_as_float(wd[q] << 16);
-          e[2 * q + 1] = __uint_as_float(wd[q] & 0xFFFF0000u);
-        }
+        unpack8(*reinterpret_cast<const uint4*>(mixed + (size_t)(i - Kw) * p.conv_dim), e);
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += p.conv_weight[(size_t)(c + q) * p.K_win + j] * e[q];
+      for (int q = 0; q < 8; ++q) win[q][j] = e[q];
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) y[q] = acc[q] * sigmoidf_(acc[q]);
+    __bf16* dst;
+    size_t dstride;
     if (c < p.key_dim) {
       const int h = c / p.Dk, d = c - h * p.Dk;
-      dst = static_cast<__bf16*>(p.q) + (((size_t)b * p.Hk + h) * p.S + t) * p.Dk + d;
+      dst = static_cast<__bf16*>(p.q) + (((size_t)b * p.Hk + h) * p.S) * p.Dk + d;
+      dstride = p.Dk;
     } else if (c < 2 * p.key_dim) {
       const int cc = c - p.key_dim, h = cc / p.Dk, d = cc - h * p.Dk;
-      dst = static_cast<__bf16*>(p.k) + (((size_t)b * p.Hk + h) * p.S + t) * p.Dk + d;
+      dst = static_cast<__bf16*>(p.k) + (((size_t)b * p.Hk + h) * p.S) * p.Dk + d;
+      dstride = p.Dk;
     } else {
       const int cc = c - 2 * p.key_dim, h = cc / p.Dv, d = cc - h * p.Dv;
-      dst = static_cast<__bf16*>(p.v) + (((size_t)b * p.Hv + h) * p.S + t) * p.Dv + d;
+      dst = static_cast<__bf16*>(p.v) + (((size_t)b * p.Hv + h) * p.S) * p.Dv + d;
+      dstride = p.Dv;
     }
-  } else {
-    const int cc = c - p.conv_dim, h = cc / p.Dv, d = cc - h * p.Dv;
-    const __bf16* zt = static_cast<const __bf16*>(p.z_tok) + tok * p.value_dim + cc;
-    *reinterpret_cast<uint4*>(static_cast<__bf16*>(p.z_head) + (((size_t)b * p.Hv + h) * p.S + t) * p.Dv + d) =
-        *reinterpret_cast<const uint4*>(zt);
-    return;
-  }
-  bf16x8 f;
+    uint4 rows[kConvTok];  // the block's token rows, all requested before the first use
 #pragma unroll
-  for (int q = 0; q < 8; ++q) f[q] = f2bf(y[q]);
-  *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, f);
+    for (int u = 0; u < kConvTok; ++u)
+      rows[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(mixed + (size_t)(t0 + u) * p.conv_dim)
+                            : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kConvTok; ++u) {
+      const int t = t0 + u;
+      if (t >= t1) break;
+      // newest entry t + Kw is token t
+      float e[8];
+      unpack8(rows[u], e);
+      bf16x8 f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) acc += wt[q][j] * (j == KW - 1 ? e[q] : win[q][j]);
+        f[q] = f2bf(acc * sigmoidf_(acc));
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)t * dstride) = __builtin_bit_cast(uint4, f);
+      // slide: slots 0 .. Kw-2 take entries t+2 .. t+Kw
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+#pragma unroll
+        for (int j = 0; j + 1 < KW - 1; ++j) win[q][j] = win[q][j + 1];
+        if constexpr (KW >= 2) win[q][KW - 2] = e[q];  // the newest entry
+      }
+    }
+  } else if (grp < gconv + gz) {
+    const int cc = 8 * (grp - gconv), h = cc / p.Dv, d = cc - h * p.Dv;
+    const __bf16* zt = static_cast<const __bf16*>(p.z_tok) + (size_t)b * p.S * p.value_dim + cc;
+    __bf16* zh = static_cast<__bf16*>(p.z_head) + (((size_t)b * p.Hv + h) * p.S) * p.Dv + d;
+    for (int t = t0; t < t1; ++t)
+      *reinterpret_cast<uint4*>(zh + (size_t)t * p.Dv) = *reinterpret_cast<const uint4*>(zt + (size_t)t * p.value_dim);
+  } else {
+    // a or b: 8 heads x the token block, [B*S, Hv] bf16 -> [B, Hv, S] fp32
+    const int g = grp - gconv - gz, which = g / ((p.Hv + 7) / 8), h0 = 8 * (g % ((p.Hv + 7) / 8));
+    const __bf16* src = static_cast<const __bf16*>(p.ab_tok) + (size_t)which * p.B * p.S * p.Hv +
+                        (size_t)b * p.S * p.Hv;
+    float* out = which ? p.b_head : p.a_head;
+    for (int q = 0; q < 8 && h0 + q < p.Hv; ++q)
+      for (int t = t0; t < t1; ++t)
+        out[((size_t)b * p.Hv + h0 + q) * p.S + t] = bf2f(src[(size_t)t * p.Hv + h0 + q]);
+  }
 }
 
 // the window after the last token: the last K_win entries of [window | tokens]
@@ -243,8 +310,9 @@ __global__ __launch_bounds__(kGThreads) void conv_window_kernel(const ConvSplitP
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t stream) {
-  if (g.M == 0 || g.N == 0) return hipSuccess;
-  const long tiles = (long)((g.M + kGBM - 1) / kGBM) * ((g.N + kGBN - 1) / kGBN);
+  long tiles = 0;
+  for (int i = 0; i < g.nprob; ++i) tiles += (long)((g.M + kGBM - 1) / kGBM) * ((g.N[i] + kGBN - 1) / kGBN);
+  if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(kGThreads), 0, stream, g);
   return hipGetLastError();
 }
@@ -258,10 +326,21 @@ hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
-  const long n = (long)p.B * p.S * ((p.conv_dim + p.value_dim) / 8);
-  if (n > 0)
-    hipLaunchKernelGGL(conv_split_kernel, dim3((unsigned)((n + kGThreads - 1) / kGThreads)), dim3(kGThreads), 0,
-                       stream, p);
+  const int gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
+  const long n = (long)p.B * ((p.S + kConvTok - 1) / kConvTok) * ((p.conv_dim + p.value_dim) / 8 + gab);
+  if (n > 0) {
+    const dim3 grid((unsigned)((n + kGThreads - 1) / kGThreads)), block(kGThreads);
+    switch (p.K_win) {
+      case 1: hipLaunchKernelGGL(conv_split_kernel<1>, grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL(conv_split_kernel<2>, grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL(conv_split_kernel<3>, grid, block, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL(conv_split_kernel<4>, grid, block, 0, stream, p); break;
+      case 5: hipLaunchKernelGGL(conv_split_kernel<5>, grid, block, 0, stream, p); break;
+      case 6: hipLaunchKernelGGL(conv_split_kernel<6>, grid, block, 0, stream, p); break;
+      case 7: hipLaunchKernelGGL(conv_split_kernel<7>, grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL(conv_split_kernel<8>, grid, block, 0, stream, p); break;
+    }
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long nw = (long)p.B * p.conv_dim;

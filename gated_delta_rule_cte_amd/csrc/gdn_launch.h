@@ -93,11 +93,14 @@ hipError_t launch_fused_pre(const FusedPre& f, int dtype, hipStream_t stream);
 hipError_t launch_fused_post(const FusedPost& f, int dtype, hipStream_t stream);
 
 // ----------------------------------------------- prefill layer (bf16 only)
+// up to four products sharing the left operand, C_p[M, N_p] = A[M, K] B_p[K, N_p]
+// (bf16 row-major, N_p % 8 == 0, K % 64 == 0), in one launch
 struct GemmParams {
-  const void* A;  // [M, K] bf16 row-major
-  const void* B;  // [K, N] bf16 row-major
-  void* C;        // [M, N] bf16 row-major
-  int M, N, K;    // K % 64 == 0
+  const void* A;
+  int M, K, nprob;
+  const void* B[4];
+  void* C[4];
+  int N[4];
 };
 hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t stream);
 struct NarrowParams {
@@ -119,6 +122,11 @@ struct ConvSplitParams {
   void* k;
   void* v;                   // [B, Hv, S, Dv] bf16
   void* z_head;              // [B, Hv, S, Dv] bf16
+  // when not NULL: the a and b projections token-major, [2][B * S, Hv] bf16,
+  // moved to a_head / b_head ([B, Hv, S] fp32)
+  const void* ab_tok;
+  float* a_head;
+  float* b_head;
   int B, S, conv_dim, value_dim, key_dim, Hk, Hv, Dk, Dv, K_win;
 };
 hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream);
