@@ -144,6 +144,7 @@ BLOCK_CTE_CASES = [
     (1, 300, 256, 1, 2, 64, 64, 3, True, 0),
     (1, 2, 128, 2, 2, 16, 24, 4, True, 0),      # fewer tokens than the conv window
     (1, 130, 128, 2, 2, 128, 128, 4, False, 1),  # full head dims, Neumann inverse
+    (2, 70, 256, 4, 8, 32, 32, 4, True, 0),      # Hv % 8 == 0: a and b on the GEMM
 ]
 
 
