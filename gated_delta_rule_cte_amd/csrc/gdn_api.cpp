@@ -174,7 +174,7 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
     if (int r = check_disjoint(ws, {q, k, v, g, be, st, o})) return r;
   }
   if (int r = check_device()) return r;
-  gdn::CteParams p;
+  gdn::CteParams p{};
   p.q = query; p.k = key; p.v = value; p.g = g_log; p.beta = beta;
   p.state = recurrent_state; p.out = out;
   p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
@@ -262,9 +262,16 @@ int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, c
   f.rows_qk = (long)B * Hk * S;
   f.tokens_v = (long)B * Hv * S;
   f.S = S; f.Hv = Hv; f.Dk = Dk;
-  hipError_t e = gdn::launch_fused_pre(f, dtype, hs);
-  if (e != hipSuccess) return launched(e);
-  gdn::CteParams p;
+  gdn::CteParams p{};
+  hipError_t e = hipSuccess;
+  if (dtype == GDN_BF16) {
+    // bf16: the chunk-local kernel forms the unit rows and the gates itself
+    // (into the same workspace areas), so no separate passes run
+    p.q_raw = q; p.k_raw = k; p.b_raw = b; p.a_raw = a; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.qn = f.qn; p.kn = f.kn; p.g_out = f.g; p.beta_out = f.beta;
+  } else if ((e = gdn::launch_fused_pre(f, dtype, hs)) != hipSuccess) {
+    return launched(e);
+  }
   p.q = f.qn; p.k = f.kn; p.v = v; p.g = f.g; p.beta = f.beta;
   p.state = recurrent_state; p.out = out;
   p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;
@@ -414,8 +421,15 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   f.g = reinterpret_cast<float*>(w + L.g); f.beta = reinterpret_cast<float*>(w + L.beta);
   f.rows_qk = (long)B * Hk * S; f.tokens_v = (long)B * Hv * S;
   f.S = S; f.Hv = Hv; f.Dk = Dk;
-  if ((e = gdn::launch_fused_pre(f, GDN_BF16, hs)) != hipSuccess) return launched(e);
-  gdn::CteParams p;
+  gdn::CteParams p{};
+  if (gdn::fused_inplace_ok(Hk, Hv)) {
+    // the chunk-local kernel forms the unit rows over the raw ones (one wave
+    // reads and writes each key head's chunk) and the gates
+    p.q_raw = f.q; p.k_raw = f.k; p.b_raw = f.b; p.a_raw = f.a; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.qn = f.qn; p.kn = f.kn; p.g_out = f.g; p.beta_out = f.beta;
+  } else if ((e = gdn::launch_fused_pre(f, GDN_BF16, hs)) != hipSuccess) {
+    return launched(e);
+  }
   p.q = w + L.q; p.k = w + L.k; p.v = w + L.v; p.g = f.g; p.beta = f.beta;
   p.state = recurrent_state_out; p.out = w + L.o;
   p.B = B; p.Hk = Hk; p.Hv = Hv; p.S = S; p.Dk = Dk; p.Dv = Dv;

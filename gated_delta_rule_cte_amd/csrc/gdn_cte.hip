@@ -39,6 +39,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kC = 64;        // chunk length (one 16-row block per wave)
 constexpr int kNB = kC / 16;  // 16-token blocks per chunk
 constexpr int kAlgoNeumann = 1;  // intra-chunk inverse by the doubling Neumann product
+constexpr float kL2Eps = 1e-6f;   // l2norm(x) = x / sqrt(sum x^2 + kL2Eps) in the folded prologue
 
 #ifdef GDN_CTE_PROFILE
 constexpr int kProfSlots = 16;
@@ -392,6 +393,11 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
 // ===========================================================================
 // The same chunk-local products as above with no workgroup barrier: one
 // wave computes a whole chunk, so many chunks are in flight per CU.
+//  - With FUSE the decode step's prologue runs here first (the "GDN TKG
+//    Kernel API Reference" summary: l2norm of q and k, beta = sigmoid(b),
+//    g = -exp(A_log) softplus(a + dt_bias)): raw rows are made unit length in
+//    the fragments and written once per key head and chunk for the state
+//    pass, with beta and g.
 //  - K and Q arrive straight from HBM as MFMA fragments (16 bytes per lane).
 //  - A and P are produced transposed (the K rows of block j as the first
 //    operand), so a lane holds 4 consecutive columns of one row and writes
@@ -423,7 +429,9 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
 
 // NG value heads that share a key head (GQA) per wave: the raw K K^T and
 // Q K^T products are the same for all of them; only beta and the decays differ.
-template <int DK, int NG, int ALGO>
+// FUSE: the decode step's prologue is folded in (raw q, k and gates in; unit
+// rows of q, k and beta, g out for the state pass), see CteParams.
+template <int DK, int NG, int ALGO, bool FUSE>
 __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
@@ -456,23 +464,86 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   const uint32_t rem = (uint32_t)(S - c0);
 
   // K, Q fragments of all four row blocks; g, beta (lane = token)
-  const auto rK = make_rsrc(static_cast<const T*>(p.k) + ((size_t)(b * Hk + hk) * S + c0) * Dk, rem * Dk * 2u);
-  const auto rQ = make_rsrc(static_cast<const T*>(p.q) + ((size_t)(b * Hk + hk) * S + c0) * Dk, rem * Dk * 2u);
+  const size_t qk0 = ((size_t)(b * Hk + hk) * S + c0) * Dk;  // this chunk's first q / k element
+  const auto rK = make_rsrc(static_cast<const T*>(FUSE ? p.k_raw : p.k) + qk0, rem * Dk * 2u);
+  const auto rQ = make_rsrc(static_cast<const T*>(FUSE ? p.q_raw : p.q) + qk0, rem * Dk * 2u);
   V8 kf[NB][NS], qf[NB][NS];
+  uint32_t foff[NS];  // byte offset of fragment s in row block 0 (row stride Dk * 2)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int k8 = 32 * s + 8 * lg;
+    foff[s] = k8 < Dk ? (uint32_t)(lr * Dk + k8) * 2u : kOOB;
+  }
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int k8 = 32 * s + 8 * lg;
-      const uint32_t off = k8 < Dk ? (uint32_t)((16 * rb + lr) * Dk + k8) * 2u : kOOB;
+      const uint32_t off = foff[s] == kOOB ? kOOB : foff[s] + (uint32_t)(16 * rb * Dk) * 2u;
       kf[rb][s] = V8::bload(rK, off);
       qf[rb][s] = V8::bload(rQ, off);
     }
   float gln[NG], ben[NG];
+  if constexpr (FUSE) {
+    // Each row made unit length: lane (lr, lg) holds 8 columns of row
+    // 16 rb + lr in each of its NS fragments, the rest of the row is in lanes
+    // lr + 16 j.  One wave per key head and chunk writes the rows for the
+    // state pass.
+    auto unit_rows = [&](V8* f) {
+      float ss = 0.f;
 #pragma unroll
-  for (int n = 0; n < NG; ++n) {
-    gln[n] = buf_load_f32(make_rsrc(p.g + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
-    ben[n] = buf_load_f32(make_rsrc(p.beta + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[s].get(e) * f[s].get(e);
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      const float inv = 1.0f / sqrtf(ss + kL2Eps);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = f2bf(f[s].get(e) * inv);
+        f[s].u = __builtin_bit_cast(uint4, y);
+      }
+    };
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      unit_rows(kf[rb]);
+      unit_rows(qf[rb]);
+    }
+    if (hh0 == 0) {
+      const auto wK = make_rsrc(static_cast<T*>(p.kn) + qk0, rem * Dk * 2u);
+      const auto wQ = make_rsrc(static_cast<T*>(p.qn) + qk0, rem * Dk * 2u);
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const uint32_t off = foff[s] == kOOB ? kOOB : foff[s] + (uint32_t)(16 * rb * Dk) * 2u;
+          kf[rb][s].bstore(wK, off);
+          qf[rb][s].bstore(wQ, off);
+        }
+    }
+    // beta = sigmoid(b), g = -exp(A_log[h]) softplus(a + dt_bias[h]) for the
+    // token of this lane; zero past the sequence end
+    const bool tv = c0 + lane < S;
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+      const size_t row = (size_t)(bh0 + n) * S + c0;
+      const int h = (bh0 + n) % Hv;
+      const float bb = buf_load_f32(make_rsrc(p.b_raw + row, rem * 4u), (uint32_t)lane * 4u);
+      const float aa = buf_load_f32(make_rsrc(p.a_raw + row, rem * 4u), (uint32_t)lane * 4u);
+      gln[n] = tv ? -expf(p.A_log[h]) * softplusf_(aa + p.dt_bias[h]) : 0.f;
+      ben[n] = tv ? sigmoidf_(bb) : 0.f;
+      if (tv) {
+        p.g_out[row + lane] = gln[n];
+        p.beta_out[row + lane] = ben[n];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+      gln[n] = buf_load_f32(make_rsrc(p.g + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+      ben[n] = buf_load_f32(make_rsrc(p.beta + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+    }
   }
 
   // raw products of the lower blocks, transposed: lane holds row 16 i + lr,
@@ -1438,22 +1509,35 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   }
 }
 
+// one wave per (chunk, key head, pair of value heads) when the GQA group is
+// even, else per (chunk, value head)
+constexpr int local1_ng(int Hk, int Hv) { return (Hv / Hk) % 2 == 0 ? 2 : 1; }
+
+template <int DK, bool FUSE>
+hipError_t launch_local1(const CteParams& p, long grid1, hipStream_t stream) {
+  const bool neu = p.algo == kAlgoNeumann;
+  if (local1_ng(p.Hk, p.Hv) == 2) {
+    if (neu)
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
+  } else if (neu)
+    hipLaunchKernelGGL((cte_local1_kernel<DK, 1, kAlgoNeumann, FUSE>), dim3((unsigned)grid1), dim3(kWave), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL((cte_local1_kernel<DK, 1, 0, FUSE>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int DK>
 hipError_t launch_local(const CteParams& p, hipStream_t stream) {
   const long grid1 = (long)p.B * p.Hv * (p.c_end - p.c_begin);
   if (grid1 == 0) return hipSuccess;
   const bool neu = p.algo == kAlgoNeumann;
   if constexpr (sizeof(T) == 2) {
-    if ((p.Hv / p.Hk) % 2 == 0) {
-      if (neu)
-        hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0,
-                           stream, p);
-      else
-        hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
-    } else if (neu)
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 1, kAlgoNeumann>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
-    else
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 1, 0>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+    if (p.q_raw) return launch_local1<DK, true>(p, grid1, stream);
+    return launch_local1<DK, false>(p, grid1, stream);
   } else if (neu)
     hipLaunchKernelGGL((cte_local_kernel<T, DK, kAlgoNeumann>), dim3((unsigned)grid1), dim3(kThreads), 0, stream, p);
   else
@@ -1514,8 +1598,11 @@ size_t cte_workspace_bytes(int B, int Hv, int S, int dtype) {
   return (size_t)B * Hv * NC * 2 * kC * kC * (dtype == 1 ? 2 : 4);
 }
 
+bool fused_inplace_ok(int Hk, int Hv) { return Hv / Hk == local1_ng(Hk, Hv); }
+
 hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream) {
   if ((long)p.B * p.Hv == 0) return hipSuccess;
+  if (p.q_raw && dtype != 1) return hipErrorInvalidValue;  // the folded prologue is bf16 only
   const bool dk64 = p.Dk <= 64;
   if (dtype == 1) {
     const int dvt = pick_dvt(p, 64);

@@ -5,11 +5,14 @@
 // g = -exp(A_log) softplus(a + dt_bias), the 1/sqrt(K) query scale and
 // RMSNormGated(out, z)).
 //
-// Three HBM-bound row passes around the chunked prefill:
+// HBM-bound row passes around the chunked prefill:
 //   l2norm_rows_kernel    q^, k^ = x / sqrt(sum x^2 + 1e-6), rounded to the compute type;
 //   gates_kernel          beta and g per token of every value head (A_log, dt_bias by head);
 //   (gdn_cte with scale = Dk^-1/2 on q^, k^, v, g, beta)
 //   rms_gate_rows_kernel  y = w * o / sqrt(mean(o^2) + eps) * silu(z) over Dv, in place.
+// In bf16 the first two are folded into the prefill's chunk-local kernel
+// (which holds every key row of its chunk anyway); they run as passes for
+// fp32 and where that kernel cannot write the unit rows over the raw ones.
 // A row of up to 128 elements is one group of 16 lanes, 8 elements per lane,
 // reduced with lane shuffles; 16 rows per workgroup of 256 threads.
 #include "gdn_device.h"

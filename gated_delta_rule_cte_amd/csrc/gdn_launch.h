@@ -57,7 +57,27 @@ struct CteParams {
   // per-workgroup phase cycle counts, written only by builds compiled with
   // GDN_CTE_PROFILE (a development aid); NULL otherwise
   unsigned long long* prof;
+  // The decode step's prologue folded into the chunk-local kernel (bf16
+  // only; NULL q_raw = off).  That kernel then reads raw q_raw, k_raw (the
+  // layout of q, k), writes each row made unit length, x / sqrt(sum x^2 +
+  // 1e-6) rounded to bf16, to qn, kn, and writes beta = sigmoid(b_raw) and
+  // g = -exp(A_log[h]) softplus(a_raw + dt_bias[h]) per token to g_out,
+  // beta_out.  q, k, g, beta must point at qn, kn, g_out, beta_out, which
+  // the state pass reads.  qn, kn may alias q_raw, k_raw only when one wave
+  // serves all value heads of a key head (fused_inplace_ok).
+  const void* q_raw;
+  const void* k_raw;
+  const float* b_raw;
+  const float* a_raw;
+  const float* A_log;
+  const float* dt_bias;
+  void* qn;
+  void* kn;
+  float* g_out;
+  float* beta_out;
 };
+// true when the folded prologue may write its unit rows over q_raw, k_raw
+bool fused_inplace_ok(int Hk, int Hv);
 size_t cte_workspace_bytes(int B, int Hv, int S, int dtype);
 hipError_t launch_cte(const CteParams& p, int dtype, hipStream_t stream);
 

@@ -114,6 +114,9 @@ FUSED_CASES = [
     (1, 2, 4, 300, 128, 128, "bf16", True),
     (1, 1, 1, 1100, 128, 48, "bf16", False),
     (2, 2, 4, 333, 64, 64, "bf16", True),
+    # several chunk-local waves per key head: one of them writes the unit q, k rows
+    (1, 1, 4, 200, 128, 64, "bf16", True),
+    (1, 2, 6, 150, 64, 64, "bf16", False),
 ]
 
 
@@ -145,6 +148,10 @@ BLOCK_CTE_CASES = [
     (1, 2, 128, 2, 2, 16, 24, 4, True, 0),      # fewer tokens than the conv window
     (1, 130, 128, 2, 2, 128, 128, 4, False, 1),  # full head dims, Neumann inverse
     (2, 70, 256, 4, 8, 32, 32, 4, True, 0),      # Hv % 8 == 0: a and b on the GEMM
+    # GQA groups of 3 and 4: the q, k rows are normalised by a separate pass
+    # (several chunk-local waves read each key head, so none may overwrite it)
+    (1, 90, 128, 1, 3, 32, 32, 4, False, 0),
+    (1, 70, 128, 1, 4, 32, 32, 4, True, 1),
 ]
 
 
