@@ -570,7 +570,7 @@ def main():
             "timing": ("HIP graphs replayed on one stream, HIP events; a step is one graph (all three "
                        "entry points), per-entry-point times come from graphs of 16 calls"),
         },
-        "roofline": dict(rooflines[dominant], kernel={"cte": "cte_kernel", "tkg": "tkg_kernel",
+        "roofline": dict(rooflines[dominant], kernel={"cte": "cte_local1_kernel + cte_state_ws_kernel", "tkg": "tkg_kernel",
                                                       "block": "block_proj_kernel + tkg_kernel"}[dominant]),
         "cpu_baseline": cpu,
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
