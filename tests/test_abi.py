@@ -180,3 +180,79 @@ def test_binding_fails_loudly_without_library(tmp_path):
             gdn.load(str(tmp_path / "missing.so"))
     finally:
         gdn._lib = saved
+
+
+def fused_call(lib, ptrs=None, B=1, Hk=2, Hv=4, S=100, Dk=64, Dv=64, dtype=gdn.GDN_BF16, algorithm=0,
+               eps=1e-6, ws="auto", ws_bytes=None):
+    p = ptrs or addrs(11)
+    need = lib.gdn_cte_fused_workspace_size(B, Hk, Hv, S, Dk, Dv, dtype)
+    w = ctypes.c_void_p(A + 20 * STEP) if ws == "auto" else ws
+    return lib.gdn_cte_fused(*p[:10], 1, p[10], B, Hk, Hv, S, Dk, Dv, dtype, algorithm, eps, w,
+                             need if ws_bytes is None else ws_bytes, None)
+
+
+def test_cte_fused_checks(lib):
+    """gdn_cte_fused: every argument check, before any HIP call."""
+    assert fused_call(lib, dtype=9) == -3
+    assert fused_call(lib, algorithm=2) == -7
+    assert fused_call(lib, Hv=3) == -2
+    assert fused_call(lib, Dk=130) == -2
+    assert fused_call(lib, S=-1) == -2
+    assert fused_call(lib, eps=-1.0) == -2
+    bad = addrs(11)
+    bad[2] = None                                   # v
+    assert fused_call(lib, ptrs=bad) == -1
+    bad = addrs(11)
+    bad[7] = ctypes.c_void_p(bad[7].value + 4)      # z misaligned
+    assert fused_call(lib, ptrs=bad) == -4
+    bad = addrs(11)
+    bad[10] = ctypes.c_void_p(bad[0].value + 64)    # out inside q
+    assert fused_call(lib, ptrs=bad) == -5
+    bad = addrs(11)
+    bad[9] = ctypes.c_void_p(bad[3].value)          # state on top of b
+    assert fused_call(lib, ptrs=bad) == -5
+    need = lib.gdn_cte_fused_workspace_size(1, 2, 4, 100, 64, 64, gdn.GDN_BF16)
+    assert need > lib.gdn_cte_workspace_size(1, 2, 4, 100, 64, 64, gdn.GDN_BF16)
+    assert fused_call(lib, ws=None) == -6
+    assert fused_call(lib, ws_bytes=need - 1) == -6
+    assert fused_call(lib, ws=ctypes.c_void_p(A + 20 * STEP + 16)) == -4
+    assert fused_call(lib, ws=ctypes.c_void_p(A + 2 * STEP)) == -5     # on top of v
+    assert fused_call(lib) == -9                                      # valid: no device here
+    assert fused_call(lib, B=0) == 0
+
+
+def block_cte_call(lib, ptrs=None, B=2, S=16, H=128, Hk=2, Hv=4, Dk=32, Dv=32, K_win=4, algorithm=0,
+                   eps=1e-6, ws="auto", ws_bytes=None):
+    p = ptrs or addrs(14)
+    need = lib.gdn_block_cte_workspace_size(B, S, H, Hk, Hv, Dk, Dv, K_win)
+    w = ctypes.c_void_p(A + 30 * STEP) if ws == "auto" else ws
+    return lib.gdn_block_cte(*p, B, S, H, Hk, Hv, Dk, Dv, K_win, algorithm, eps, w,
+                             need if ws_bytes is None else ws_bytes, None)
+
+
+def test_block_cte_checks(lib):
+    """gdn_block_cte: every argument check, before any HIP call; the caches may
+    alias their inputs exactly but not partly."""
+    assert block_cte_call(lib, H=100) == -2
+    assert block_cte_call(lib, K_win=9) == -2
+    assert block_cte_call(lib, Hv=3) == -2
+    assert block_cte_call(lib, Dv=12) == -2
+    assert block_cte_call(lib, algorithm=5) == -7
+    bad = addrs(14)
+    bad[1] = None                                   # W_in_qkv
+    assert block_cte_call(lib, ptrs=bad) == -1
+    bad = addrs(14)
+    bad[11] = ctypes.c_void_p(bad[0].value + 32)    # out inside hidden
+    assert block_cte_call(lib, ptrs=bad) == -5
+    bad = addrs(14)
+    bad[12] = ctypes.c_void_p(bad[6].value + 16)    # conv_state_out partly over conv_state_in
+    assert block_cte_call(lib, ptrs=bad) == -5
+    inplace = addrs(14)
+    inplace[12], inplace[13] = inplace[6], inplace[10]
+    assert block_cte_call(lib, ptrs=inplace) == -9  # exact aliases are valid
+    assert block_cte_call(lib, ws=None) == -6
+    need = lib.gdn_block_cte_workspace_size(2, 16, 128, 2, 4, 32, 32, 4)
+    assert block_cte_call(lib, ws_bytes=need - 1) == -6
+    assert block_cte_call(lib, ws=ctypes.c_void_p(A + 30 * STEP + 128)) == -4
+    assert block_cte_call(lib) == -9
+    assert block_cte_call(lib, B=0) == 0
