@@ -152,6 +152,10 @@ BLOCK_CTE_CASES = [
     # (several chunk-local waves read each key head, so none may overwrite it)
     (1, 90, 128, 1, 3, 32, 32, 4, False, 0),
     (1, 70, 128, 1, 4, 32, 32, 4, True, 1),
+    # the longest conv windows the API accepts, one of them longer than the sequence
+    (1, 50, 128, 2, 4, 32, 32, 8, True, 0),
+    (2, 37, 128, 1, 2, 32, 32, 5, False, 0),
+    (1, 5, 128, 1, 1, 16, 16, 8, True, 0),
 ]
 
 
@@ -176,7 +180,12 @@ def test_block_cte_matches_oracle(gpu_lib, case):
                                      d["recurrent_state"].f64(), Hk, Hv, Dk, Dv)
     assert_close(host(out), ry, TOL_BF16, 1, "out")
     assert_close(host(rs1), rrs, TOL_BF16, 2, "recurrent state")
-    np.testing.assert_array_equal(host(cs1), rcs)
+    # the final window: entries carried over from the old window are copied bit
+    # for bit, the others are the bf16-rounded projections of the last tokens
+    win, n_new = host(cs1), min(S, W)
+    np.testing.assert_array_equal(win[..., :W - n_new], rcs[..., :W - n_new])
+    assert_bf16_sums_match(win[..., W - n_new:], rcs[..., W - n_new:], d["hidden"].f64()[:, S - n_new:],
+                           d["W_in_qkv"].f64(), "conv window")
     if in_place:
         assert cs1.data_ptr() == cs.data_ptr() and rs1.data_ptr() == rs.data_ptr()
 
@@ -414,9 +423,11 @@ def _check_block(gpu_out, d):
 
 
 # H = 1024 / 4096 take the fully unrolled K loops; B = 70 spans two batch tiles
-# with a ragged second one; Hv = 8 takes the vector a|b tile
+# with a ragged second one; Hv = 8 takes the vector a|b tile; windows of 6 and
+# 8 take the generic conv epilogue up to the longest window the API accepts
 @pytest.mark.parametrize("case", [(3, 256, 2, 4, 32, 32, 4), (5, 384, 1, 2, 64, 48, 3), (2, 128, 2, 2, 16, 16, 1),
-                                  (70, 1024, 2, 8, 32, 32, 4), (17, 4096, 1, 8, 16, 24, 2)],
+                                  (70, 1024, 2, 8, 32, 32, 4), (17, 4096, 1, 8, 16, 24, 2),
+                                  (4, 256, 2, 4, 32, 32, 8), (3, 128, 1, 2, 16, 24, 6)],
                          ids=lambda c: "B{}_H{}_Hk{}_Hv{}_Dk{}_Dv{}_W{}".format(*c))
 def test_block_small(gpu_lib, case):
     B, H, Hk, Hv, Dk, Dv, W = case
