@@ -276,17 +276,34 @@ __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitPa
     const int cc = 8 * (grp - gconv), h = cc / p.Dv, d = cc - h * p.Dv;
     const __bf16* zt = static_cast<const __bf16*>(p.z_tok) + (size_t)b * p.S * p.value_dim + cc;
     __bf16* zh = static_cast<__bf16*>(p.z_head) + (((size_t)b * p.Hv + h) * p.S) * p.Dv + d;
-    for (int t = t0; t < t1; ++t)
-      *reinterpret_cast<uint4*>(zh + (size_t)t * p.Dv) = *reinterpret_cast<const uint4*>(zt + (size_t)t * p.value_dim);
+    // every row of the block requested before the first store (the source
+    // and destination types match, so the compiler may not reorder them)
+    uint4 zr[kConvTok];
+#pragma unroll
+    for (int u = 0; u < kConvTok; ++u)
+      zr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(zt + (size_t)(t0 + u) * p.value_dim)
+                          : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kConvTok; ++u)
+      if (t0 + u < t1) *reinterpret_cast<uint4*>(zh + (size_t)(t0 + u) * p.Dv) = zr[u];
   } else {
     // a or b: 8 heads x the token block, [B*S, Hv] bf16 -> [B, Hv, S] fp32
     const int g = grp - gconv - gz, which = g / ((p.Hv + 7) / 8), h0 = 8 * (g % ((p.Hv + 7) / 8));
     const __bf16* src = static_cast<const __bf16*>(p.ab_tok) + (size_t)which * p.B * p.S * p.Hv +
                         (size_t)b * p.S * p.Hv;
     float* out = which ? p.b_head : p.a_head;
-    for (int q = 0; q < 8 && h0 + q < p.Hv; ++q)
-      for (int t = t0; t < t1; ++t)
-        out[((size_t)b * p.Hv + h0 + q) * p.S + t] = bf2f(src[(size_t)t * p.Hv + h0 + q]);
+    const int nh = min(8, p.Hv - h0);
+    float x[8][kConvTok];  // all loads before the first store
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < kConvTok; ++u)
+        x[q][u] = (q < nh && t0 + u < t1) ? bf2f(src[(size_t)(t0 + u) * p.Hv + h0 + q]) : 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < kConvTok; ++u)
+        if (q < nh && t0 + u < t1) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = x[q][u];
   }
 }
 
