@@ -270,9 +270,9 @@ def test_cte_long_batched_workload_and_chaining(gpu_lib):
 
 
 def test_cte_inside_graph_capture(gpu_lib):
-    """The segmented prefill (chunk-local work on a second stream) captured in a
-    HIP graph: every replay, with eager work and syncs between replays, equals
-    the eager call bit for bit."""
+    """The prefill (chunk-local kernel, then the state pass, on the caller's
+    stream) captured in a HIP graph: every replay, with eager work and syncs
+    between replays, equals the eager call bit for bit."""
     import torch
     d = inputs.cte_inputs(1, 2, 4, 2048 + 64 * 5 + 17, 128, 128, dtype="bf16", state_std=0.05, seed=91)
     q, k, v, g, be = (dev(d[n]) for n in ("query", "key", "value", "g_log", "beta"))
@@ -541,3 +541,92 @@ def assert_bf16_sums_match(x, ref, hidden, W, what, max_frac=1e-2):
                            f"{np.argwhere(bad)[:8].tolist()}: gpu {x[bad][:8]}, ref {ref[bad][:8]}")
     frac = float((x != ref).mean())
     assert frac <= max_frac, f"{what}: {frac:.2%} of the values differ from the oracle's rounding"
+
+
+# ---------------------------------------------------------------------------
+# graph capture of the other entry points (the library records no memset)
+# ---------------------------------------------------------------------------
+def _check_graph_replays(call, fresh, outputs, what):
+    """call() launches on the current stream and writes `outputs`; fresh()
+    restores every buffer the call updates in place.  Capture once, then replay
+    three times with eager work and syncs in between: each replay must equal
+    the eager call bit for bit."""
+    import torch
+    fresh()
+    call()
+    _sync()
+    refs = [o.clone() for o in outputs]
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fresh()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            call()
+    for _ in range(3):
+        for o in outputs:
+            o.zero_()
+        fresh()
+        _sync()
+        graph.replay()
+        _sync()
+        for o, r in zip(outputs, refs):
+            assert torch.equal(o, r), f"{what}: a graph replay differs from the eager call"
+
+
+def test_tkg_and_block_tkg_inside_graph_capture(gpu_lib):
+    """The decode step and the decode layer with their caches updated in place,
+    as a serving loop captures them."""
+    import torch
+    t = inputs.tkg_inputs(4, 8, 128, 128, seed=71)
+    names = ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "state_in")
+    a = [dev(t[n]) for n in names]
+    s0, st = a[9].clone(), a[9]
+    y = torch.empty((32, 128), dtype=torch.bfloat16, device=st.device)
+
+    def fresh():
+        st.copy_(s0)
+    _check_graph_replays(lambda: gpu_lib.gdn_tkg(*a[:9], st, state_out=st, out=y), fresh, [y, st], "gdn_tkg")
+
+    b = inputs.block_inputs(8, 512, 2, 4, 64, 64, seed=72)
+    args = [dev(b[n]) for n in BLOCK_KEYS]
+    cs0, rs0 = args[6].clone(), args[10].clone()
+    cs, rs = args[6], args[10]
+    out = torch.empty((8, 1, 4 * 64), dtype=torch.bfloat16, device=cs.device)
+
+    def fresh_b():
+        cs.copy_(cs0)
+        rs.copy_(rs0)
+    _check_graph_replays(lambda: gpu_lib.gdn_block_tkg(*args, conv_state_out=cs, recurrent_state_out=rs, out=out),
+                         fresh_b, [out, cs, rs], "gdn_block_tkg")
+
+
+def test_fused_prefill_and_prefill_layer_inside_graph_capture(gpu_lib):
+    """gdn_cte_fused (the folded prologue) and gdn_block_cte (GEMM, conv, fused
+    prefill, output norm; caches in place) captured and replayed."""
+    import torch
+    d = inputs.cte_fused_inputs(1, 2, 4, 300, 128, 128, dtype="bf16", state_std=0.05, seed=73)
+    keys = ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight")
+    a = [dev(d[n]) for n in keys]
+    s0 = dev(d["recurrent_state"])
+    st = s0.clone()
+    y = torch.empty((1, 4, 300, 128), dtype=torch.bfloat16, device=st.device)
+
+    def fresh():
+        st.copy_(s0)
+    _check_graph_replays(lambda: gpu_lib.gdn_cte_fused(*a, recurrent_state=st, out=y), fresh, [y, st],
+                         "gdn_cte_fused")
+
+    c = inputs.block_cte_inputs(1, 200, 256, 2, 4, 64, 64, K_win=4, seed=74)
+    args = [dev(c[n]) for n in ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight")]
+    cs0, rs0 = dev(c["conv_state"]), dev(c["recurrent_state"])
+    cs, rs = cs0.clone(), rs0.clone()
+    rest = [dev(c[n]) for n in ("A_log", "dt_bias", "norm_weight")]
+    out = torch.empty((1, 200, 4 * 64), dtype=torch.bfloat16, device=cs.device)
+
+    def fresh_c():
+        cs.copy_(cs0)
+        rs.copy_(rs0)
+    _check_graph_replays(lambda: gpu_lib.gdn_block_cte(*args, cs, *rest, rs, conv_state_out=cs,
+                                                       recurrent_state_out=rs, out=out),
+                         fresh_c, [out, cs, rs], "gdn_block_cte")
