@@ -76,6 +76,29 @@ def cte_flops_per_token_head(C, Dk, Dv):
     return 2.0 * (3 * C * Dk + 2 * C * Dv + 3 * Dk * Dv + C * C / 6.0)
 
 
+def cte_roofline(t, B, Hk, Hv, S, Dk, Dv, chunk=CHUNK):
+    """Roofline object of one gdn_cte call that took t seconds.  The call sits
+    near the ridge of the two floors, so `bound` names the larger one:
+    t_mfma = F(C) flops / bf16 peak, t_hbm = algorithmic bytes / 8 TB/s;
+    `floor_over_measured` = max(t_mfma, t_hbm) / t.  `achieved`, `peak` and
+    `frac` are in the bound's own unit; both fractions are given."""
+    toks = B * S
+    fl = cte_flops_per_token_head(chunk, Dk, Dv) * toks * Hv
+    by = cte_bytes(B, Hk, Hv, S, Dk, Dv)
+    t_mfma, t_hbm = fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)
+    mfma_frac, hbm_frac = t_mfma / t, t_hbm / t
+    if t_hbm >= t_mfma:
+        head = dict(bound="hbm", achieved=by / t / 1e9, peak=PEAK_HBM_GBS, unit="GB/s", frac=hbm_frac)
+    else:
+        head = dict(bound="mfma", achieved=fl / t / 1e12, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=mfma_frac)
+    return dict(head, traffic=None, algorithmic_flops=fl, algorithmic_bytes=by,
+                mfma_TFLOPs=fl / t / 1e12, mfma_frac=mfma_frac, hbm_GBs=by / t / 1e9, hbm_frac=hbm_frac,
+                t_mfma_floor_us=t_mfma * 1e6, t_hbm_floor_us=t_hbm * 1e6,
+                floor_over_measured=max(t_mfma, t_hbm) / t,
+                recurrence_flops=6.0 * Dk * Dv * toks * Hv,  # the C-free token recurrence count
+                us=t * 1e6, tokens_per_s=toks / t, chunk=chunk)
+
+
 def cte_bytes(B, Hk, Hv, S, Dk, Dv, es=2):
     # q, k read once per key head; v, out; g, beta; state in + out
     return (2 * B * Hk * S * Dk * es + 2 * B * Hv * S * Dv * es + 2 * B * Hv * S * 4
@@ -312,13 +335,183 @@ def compare_inverse(gdn, torch, dev):
                       "supplied fp32 state, S = 128 ... 16384"}, "timing": "graphs of 8 calls, HIP events"}))
 
 
+def long_prefill(gdn, torch, dev, reps=5):
+    """gdn_cte at B=4, Hk=16, Hv=32, S=16384, D=128, bf16, zero initial state:
+    the single call, and the same sequence as four chained S=4096 calls, each
+    carrying the state to the next.  Inputs drawn on the device with the
+    workload's distributions (q, k unit rows; g ~ U(-0.3, -0.005); beta ~
+    U(0.05, 0.95)); one call moves 1.6 GB, far above the 256 MB Infinity
+    Cache, so one input set suffices.  Graphs of 2 single calls / 2 chains,
+    HIP events on the replay stream."""
+    B, Hk, Hv, S, D = 4, 16, 32, 16384, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    q = torch.randn(B, Hk, S, D, device=dev, generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    k = torch.randn(B, Hk, S, D, device=dev, generator=gen)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn(B, Hv, S, D, device=dev, generator=gen).to(torch.bfloat16)
+    g = -(0.005 + 0.295 * torch.rand(B, Hv, S, device=dev, generator=gen))
+    be = 0.05 + 0.9 * torch.rand(B, Hv, S, device=dev, generator=gen)
+    out = torch.empty(B, Hv, S, D, device=dev, dtype=torch.bfloat16)
+    seg = S // 4
+    parts = [tuple(x[:, :, i * seg:(i + 1) * seg].contiguous() for x in (q, k, v, g, be)) for i in range(4)]
+    outs = [torch.empty(B, Hv, seg, D, device=dev, dtype=torch.bfloat16) for _ in range(4)]
+    scale = D ** -0.5
+
+    def single():
+        gdn.gdn_cte(q, k, v, g, be, scale, out=out)
+
+    def chained():
+        st = None
+        for i in range(4):
+            _, st = gdn.gdn_cte(*parts[i], scale, recurrent_state=st, out=outs[i])
+
+    res = {}
+    for name, fn in (("single", single), ("chained", chained)):
+        fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                fn()
+                fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            graph.replay()
+            ev0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            ev1.record(stream)
+        ev1.synchronize()
+        t = ev0.elapsed_time(ev1) * 1e-3 / (2 * reps)
+        res[name] = cte_roofline(t, B, Hk, Hv, S, D, D)
+        del graph
+    res["config"] = {"workload": "gdn_cte bf16 B=4 Hk=16 Hv=32 S=16384 Dk=Dv=128, zero initial state; "
+                     "chained = 4 calls of S=4096 carrying the state"}
+    del q, k, v, g, be, out, parts, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def calibration(torch, dev):
+    """Measured ceilings beside the published ones: a 1 GiB device-to-device
+    copy (bytes read + written per second) and the dense bf16 MFMA kernel of
+    libgdn_calib (4096 waves x 2000 x 8 v_mfma_f32_16x16x32_bf16); median of 5."""
+    import ctypes
+    import statistics
+    res = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(6):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        dst.copy_(src)
+        ev1.record()
+        ev1.synchronize()
+        ts.append(ev0.elapsed_time(ev1) * 1e-3)
+    res["copy_GBs"] = 2 * n / statistics.median(ts[1:]) / 1e9
+    del src, dst
+    from gated_delta_rule_cte_amd import build as gbuild
+    lib = ctypes.CDLL(gbuild.CALIB_LIB)
+    lib.gdn_calib_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gdn_calib_mfma_bf16.restype = ctypes.c_int
+    lib.gdn_calib_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.gdn_calib_mfma_bf16_flops.restype = ctypes.c_double
+    waves, iters = 4096, 2000
+    sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ts = []
+    for _ in range(6):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        rc = lib.gdn_calib_mfma_bf16(waves, iters, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+        ev1.record(stream)
+        ev1.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"gdn_calib_mfma_bf16 failed ({rc})")
+        ts.append(ev0.elapsed_time(ev1) * 1e-3)
+    res["mfma_bf16_TFLOPs"] = lib.gdn_calib_mfma_bf16_flops(waves, iters) / statistics.median(ts[1:]) / 1e12
+    res["published"] = {"hbm_GBs": PEAK_HBM_GBS, "mfma_bf16_TFLOPs": PEAK_BF16_TFLOPS}
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baselines(inputs, budget_s=(10.0, 4.0, 4.0)):
+    """The oracle, as it stands, timed on the host cores on the bench's own
+    workloads (bounded samples): the float64 token-by-token C twin for the
+    prefill (OpenMP over heads) and the decode step; the numpy oracle for the
+    decode layer.  Whole-workload passes until each budget of wall time."""
+    from oracle import c_ref, gdn_ref
+    threads = c_ref.num_threads()
+    out = {}
+
+    def passes(fn, budget, cap):
+        reps, t0 = 0, time.time()
+        while reps < cap and (reps == 0 or time.time() - t0 < budget):
+            fn()
+            reps += 1
+        return reps, time.time() - t0
+
+    d = inputs.workload_inputs("cte_bf16_b1_hk16_hv32_s4096_d128")
+    a = [d[k].f64() for k in ("query", "key", "value", "g_log", "beta", "recurrent_state")]
+    reps, dt = passes(lambda: c_ref.cte(a[0], a[1], a[2], a[3], a[4], d["scale"], a[5]), budget_s[0], 60)
+    out["prefill"] = dict(value=reps * CTE["B"] * CTE["S"] / dt, unit="tokens/s", cores=threads, kind="oracle",
+                          sample=(f"{reps} passes of the whole prefill workload (B=1, 32 value heads, S=4096, "
+                                  f"D=128) through the float64 token-by-token C oracle, OpenMP over heads; "
+                                  f"{dt:.1f} s wall"))
+    t = inputs.workload_inputs("tkg_b32_hv32_d128")
+    names = ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "state_in")
+    ta = [t[n].f64() for n in names]
+    reps, dt = passes(lambda: c_ref.tkg_unrounded(*ta, t["num_v_heads"]), budget_s[1], 400)
+    us = dt / reps * 1e6
+    by = tkg_bytes(TKG["B"] * TKG["Hv"], TKG["Hv"], TKG["K"], TKG["V"])
+    out["decode_step"] = dict(value=us, unit="us/step", GB_per_s=by / (us * 1e-6) / 1e9, cores=threads,
+                              kind="oracle",
+                              sample=(f"{reps} whole decode steps (BH=1024, K=V=128) through the float64 C oracle, "
+                                      f"OpenMP over heads; {dt:.1f} s wall"))
+    b = inputs.workload_inputs("block_b64_h2048_hk16_hv32_d128")
+    keys = ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight", "conv_state", "A_log",
+            "dt_bias", "norm_weight", "recurrent_state")
+    ba = [b[n].f64() for n in keys]
+    reps, dt = passes(lambda: gdn_ref.block_tkg(*ba, b["num_k_heads"], b["num_v_heads"], b["head_k_dim"],
+                                                b["head_v_dim"]), budget_s[2], 100)
+    us = dt / reps * 1e6
+    by = block_bytes(**BLK)
+    out["decode_layer"] = dict(value=us, unit="us/step", GB_per_s=by / (us * 1e-6) / 1e9,
+                               cores=os.cpu_count(), kind="oracle",
+                               sample=(f"{reps} whole decode-layer steps (B=64, H=2048, Hk=16, Hv=32, D=128) "
+                                       f"through the float64 numpy oracle (BLAS in_proj); {dt:.1f} s wall"))
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op-iters", type=int, default=200, help="calls per entry point for per-op times")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baselines")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the B=4, S=16384 prefill (single call and 4 x 4096 chain)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measured copy-bandwidth and MFMA ceilings")
     ap.add_argument("--only", choices=["cte", "tkg", "block"], default=None,
                     help="run only one entry point's graphs (for profiler runs)")
     ap.add_argument("--eager", type=int, default=0, metavar="N",
@@ -506,15 +699,7 @@ def main():
     # ---------------------------------------------------------- rooflines
     rooflines = {}
     if run_cte:
-        t = per_op_ms["cte"] * 1e-3
-        toks = CTE["B"] * CTE["S"]
-        fl = cte_flops_per_token_head(CHUNK, CTE["Dk"], CTE["Dv"]) * toks * CTE["Hv"]
-        by = cte_bytes(**CTE)
-        rooflines["cte"] = dict(bound="mfma", achieved=fl / t / 1e12, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                                frac=fl / t / 1e12 / PEAK_BF16_TFLOPS, traffic=None,
-                                algorithmic_flops=fl, algorithmic_bytes=by,
-                                hbm_GBs=by / t / 1e9, hbm_frac=by / t / 1e9 / PEAK_HBM_GBS,
-                                us=t * 1e6, tokens_per_s=toks / t, chunk=CHUNK)
+        rooflines["cte"] = cte_roofline(per_op_ms["cte"] * 1e-3, **CTE)
     if run_tkg:
         t = per_op_ms["tkg"] * 1e-3
         by = tkg_bytes(TKG["B"] * TKG["Hv"], TKG["Hv"], TKG["K"], TKG["V"])
@@ -532,22 +717,21 @@ def main():
         r["traffic"] = traffic.get(op)
     dominant = max(per_op_ms, key=per_op_ms.get)
 
-    # ------------------------------------------------------- CPU baseline
-    cpu = None
-    if run_cte and not args.no_cpu_baseline:
-        from oracle import c_ref
-        d = inputs.workload_inputs("cte_bf16_b1_hk16_hv32_s4096_d128")
-        a = [d[k].f64() for k in ("query", "key", "value", "g_log", "beta", "recurrent_state")]
-        # whole-workload passes until about 10 s of wall time (bounded at 60 passes)
-        reps, t0 = 0, time.time()
-        while reps < 60 and (reps == 0 or time.time() - t0 < 10.0):
-            c_ref.cte(a[0], a[1], a[2], a[3], a[4], d["scale"], a[5])
-            reps += 1
-        dt = time.time() - t0
-        cpu = dict(value=reps * CTE["B"] * CTE["S"] / dt, unit="tokens/s", cores=c_ref.num_threads(),
-                   kind="oracle",
-                   sample=(f"{reps} passes of the whole prefill workload (B=1, 32 value heads, S=4096, D=128) "
-                           f"through the float64 token-by-token C oracle, OpenMP over heads; {dt:.1f} s wall"))
+    # ---------------------------------- long prefill, ceilings, CPU baselines
+    extra = {}
+    if run_cte and args.only is None and not args.no_long:
+        extra["cte_long"] = long_prefill(gdn, torch, dev)
+        traffic_long = load_traffic().get("cte_long")
+        for r in (extra["cte_long"]["single"],):
+            r["traffic"] = traffic_long
+    calib = None
+    if args.only is None and not args.no_calibration:
+        calib = calibration(torch, dev)
+    cpu, cpus = None, None
+    if args.only is None and not args.no_cpu_baseline:
+        cpus = cpu_baselines(inputs)
+        cpu = cpus["prefill"]
+    host = {"cpu_model": cpu_model(), "cpu_count": os.cpu_count()}
 
     res = {
         "metric": "GDN prefill tokens/s at S=4096; decode step us + HBM GB/s at B*Hv=1024",
@@ -577,6 +761,10 @@ def main():
         "rooflines": rooflines,
         "decode": ({"us_per_step": rooflines["tkg"]["us"], "GB_per_s": rooflines["tkg"]["achieved"],
                     "frac_of_8TBs": rooflines["tkg"]["frac"]} if run_tkg else None),
+        "cpu_baselines": cpus,
+        "calibration": calib,
+        "host": host,
+        "extra_workloads": extra or None,
         "context": ("the pages report only relative figures: their default intra-chunk inverse is "
                     "1.8x faster than the alternative at S=128 and ~3.7x at S>=2048, on Trainium"),
         "setup_s": round(t_gen, 1),

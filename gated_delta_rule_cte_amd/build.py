@@ -20,6 +20,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_tkg.hip", "gdn_cte.hip", "gdn_block.hip", "gdn_fused.hip", "gdn_block_cte.hip"]
+# measurement aids for bench.py, in a library of their own
+CALIB_LIB = os.path.join(PKG, "libgdn_calib.so")
+CALIB_SOURCES = ["gdn_calib.hip"]
+# files whose MFMA accumulators stay in VGPRs (no per-iteration AGPR copies)
+VGPR_MFMA = {"gdn_calib.hip"}
 ARCH = "gfx950"
 
 
@@ -38,13 +43,21 @@ def compile_flags(extra=()):
 
 
 def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
+    _link(SOURCES, out, verbose, extra_flags)
+    if out == LIB:
+        _link(CALIB_SOURCES, CALIB_LIB, verbose, extra_flags)
+    return out
+
+
+def _link(sources, out, verbose, extra_flags):
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
 
     def one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *compile_flags(extra_flags), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        vg = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] if src in VGPR_MFMA else []
+        cmd = [cc, *compile_flags(extra_flags), *vg, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,15 +69,14 @@ def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
             print(msgs, flush=True)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(one, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        objs = list(ex.map(one, sources))
     tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, out)
-    return out
 
 
 if __name__ == "__main__":

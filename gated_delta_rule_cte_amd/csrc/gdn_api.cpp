@@ -182,7 +182,6 @@ int gdn_cte(const void* query, const void* key, const void* value, const float* 
   p.scale = scale;
   p.algo = algorithm;
   p.ws = workspace;
-  p.prof = nullptr;
   return launched(gdn::launch_cte(p, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -279,7 +278,6 @@ int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, c
   p.scale = 1.0f / sqrtf((float)Dk);
   p.algo = algorithm;
   p.ws = S > 0 ? w + L.cte : nullptr;
-  p.prof = nullptr;
   e = gdn::launch_cte(p, dtype, hs);
   if (e != hipSuccess) return launched(e);
   gdn::FusedPost post{};
@@ -437,7 +435,6 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   p.scale = 1.0f / sqrtf((float)Dk);
   p.algo = algorithm;
   p.ws = w + L.cte;
-  p.prof = nullptr;
   if ((e = gdn::launch_cte(p, GDN_BF16, hs)) != hipSuccess) return launched(e);
   gdn::FusedPost post{};
   post.out = w + L.o; post.z = w + L.zh; post.norm_weight = norm_weight;

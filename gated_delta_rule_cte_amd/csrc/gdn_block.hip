@@ -29,10 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBM = 64;     // batch rows per workgroup (one 16-row block per wave)
-#ifndef GDN_BLOCK_BN
-#define GDN_BLOCK_BN 32
-#endif
-constexpr int kBN = GDN_BLOCK_BN;  // output columns per workgroup
+constexpr int kBN = 32;     // output columns per workgroup
 constexpr int kBK = 128;    // hidden-dimension step
 constexpr int kRing = 4;    // K tiles in flight per workgroup (register ring)
 static_assert(kRing % 2 == 0, "LDS double buffer index = ring slot parity");

@@ -41,31 +41,6 @@ constexpr int kNB = kC / 16;  // 16-token blocks per chunk
 constexpr int kAlgoNeumann = 1;  // intra-chunk inverse by the doubling Neumann product
 constexpr float kL2Eps = 1e-6f;   // l2norm(x) = x / sqrt(sum x^2 + kL2Eps) in the folded prologue
 
-#ifdef GDN_CTE_PROFILE
-constexpr int kProfSlots = 16;
-#define PROF_MARK_AT(i, who)                                      \
-  if (tid == (who)) {                                             \
-    const unsigned long long now_ = __builtin_readcyclecounter(); \
-    prof_acc[i] += now_ - prof_last;                              \
-    prof_last = now_;                                             \
-  }
-#define PROF_MARK(i) PROF_MARK_AT(i, 0)
-#else
-#define PROF_MARK_AT(i, who)
-#define PROF_MARK(i)
-#endif
-
-#ifdef GDN_CTE_PROFILE_LOCAL
-#define LPROF(i)                                                  \
-  if (tid == 0) {                                                 \
-    const unsigned long long now_ = __builtin_readcyclecounter(); \
-    lprof[i] += now_ - lprof_last;                                \
-    lprof_last = now_;                                            \
-  }
-#else
-#define LPROF(i)
-#endif
-
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -154,10 +129,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
   const int c0 = c * C, nvalid = min(C, S - c0);
   const float scale = p.scale;
 
-#ifdef GDN_CTE_PROFILE_LOCAL
-  unsigned long long lprof[8] = {};
-  unsigned long long lprof_last = __builtin_readcyclecounter();
-#endif
   // K, Q chunk tiles (all loads issued before the first store); g, beta
   {
     const T* kg = static_cast<const T*>(p.k) + ((size_t)(b * Hk + hk) * S + c0) * Dk;
@@ -187,7 +158,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();
-  LPROF(0)
 
   // raw K K^T for row block w and Q K^T for row block NB-1-w (lower blocks)
   const int rk = w, rq = NB - 1 - w;
@@ -210,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();  // K, Q tiles are dead from here on
-  LPROF(1)
 
   // decays: A (fp32) into the K tile's bytes, P (compute type) into the Q tile's
   {
@@ -248,7 +217,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
   __syncthreads();
-  LPROF(2)
 
   if constexpr (ALGO == kAlgoNeumann) {
     // T = (I - A)(I + A^2)(I + A^4) ... (I + A^32), as in the bf16 kernel:
@@ -327,7 +295,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
       for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LDA + 16 * blk + j] = tc[i];
     }
     __syncthreads();
-    LPROF(3)
 
     // off-diagonal blocks, one level (block distance d) at a time
 #pragma unroll
@@ -357,7 +324,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     }
   }
 
-  LPROF(4)
   // T (lower blocks, rounded to the compute type) and P -> workspace, 16-byte stores
   T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
   T* Pg = Tg + C * C;
@@ -381,11 +347,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
     v.store(Tg + t * C + c8);
     V8::load(sPs + t * LDC + c8).store(Pg + t * C + c8);
   }
-  LPROF(5)
-#ifdef GDN_CTE_PROFILE_LOCAL
-  if (tid == 0 && p.prof)
-    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * 16 + i] = lprof[i];
-#endif
 }
 
 // ===========================================================================
@@ -445,10 +406,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
 
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int tid = lane;
-#ifdef GDN_CTE_PROFILE_LOCAL
-  unsigned long long lprof[8] = {};
-  unsigned long long lprof_last = __builtin_readcyclecounter();
-#endif
   const int S = p.S, Dk = p.Dk, Hk = p.Hk, Hv = p.Hv;
   const int NC = (S + C - 1) / C;
   const int G = Hv / Hk;
@@ -571,7 +528,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   sGam[lane] = wave_inclusive_scan_dpp(gln[n]);
   sBeta[lane] = ben[n];
   wave_lds_sync();
-  LPROF(0)
 
   // A (packed, fp32) and P (registers)
   f4 pacc[kNTri];
@@ -596,7 +552,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
     }
   }
   wave_lds_sync();
-  LPROF(1)
 
   if constexpr (ALGO == kAlgoNeumann) {
     // T = (I - A)(I + A^2)(I + A^4) ... (I + A^32): with Pw the running power
@@ -655,7 +610,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       put(sTb, tb);
       wave_lds_sync();
     }
-    LPROF(2)
   } else {
     // diagonal blocks of T: lane = (block, column), forward substitution
     {
@@ -682,7 +636,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       for (int i = 0; i < 16; ++i) Tb[i * kLB + j] = tc[i];
     }
     wave_lds_sync();
-    LPROF(2)
 
     // T blocks in the accumulator layout (lane: rows 4 lg + r, column lr)
     f4 tb[kNTri];
@@ -714,7 +667,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   // P (bf16) into the A area, which the levels above no longer read
   T* sP = reinterpret_cast<T*>(sA);
   wave_lds_sync();
-  LPROF(3)
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -743,11 +695,6 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
     *reinterpret_cast<uint4*>(Pg + go) = *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
   }
   }  // value heads
-  LPROF(4)
-#ifdef GDN_CTE_PROFILE_LOCAL
-  if (tid == 0 && p.prof)
-    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * 16 + i] = lprof[i];
-#endif
 }
 
 // ===========================================================================
@@ -837,10 +784,6 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
     store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hacc[j][0], hacc[j][1], hacc[j][2], hacc[j][3]);
   }
 
-#ifdef GDN_CTE_PROFILE
-  unsigned long long prof_acc[kProfSlots] = {};
-  unsigned long long prof_last = __builtin_readcyclecounter();
-#endif
 
   // ---- loop-invariant per-thread offsets (bytes from the chunk start)
   // K: item i = rows t0, t0+1 (t0 = 2 tp) at columns c8..c8+7
@@ -909,10 +852,6 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
   //      and registers (Q, T, P fragments)
   V8 qf[NQ], tf[KSTEPS], pf[KSTEPS];
   auto stage = [&](int c) {
-#ifdef GDN_CTE_PROFILE
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): time the wait for the prefetch on its own
-    PROF_MARK(5)
-#endif
     T* sK = sKb[c & 1];
 #pragma unroll
     for (int i = 0; i < NKI; ++i) {
@@ -957,7 +896,6 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
   __syncthreads();
 
   for (int c = 0; c < NC; ++c) {
-    PROF_MARK(0)
     // ------------------------------------------------------------------- B
     if (c > 0) flush_out(c - 1);
     f4 oacc[NVB];
@@ -999,7 +937,6 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
       }
     }
     __syncthreads();
-    PROF_MARK(1)
 
     // ------------------------------------------------------------------- C
 #pragma unroll
@@ -1013,7 +950,6 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
       store4<T>(sUd + off, dt[0] * u[0], dt[1] * u[1], dt[2] * u[2], dt[3] * u[3]);
     }
     __syncthreads();
-    PROF_MARK(2)
 
     // ------------------------------------------------------------------- D
 #pragma unroll
@@ -1040,23 +976,14 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
         store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
       }
     }
-    PROF_MARK(3)
     if (c + 1 < NC) {
       stage(c + 1);
-      PROF_MARK(6)
       if (c + 2 < NC) prefetch(c + 2);
-      PROF_MARK(7)
     }
     __syncthreads();
-    PROF_MARK(4)
   }
   if (NC > 0) flush_out(NC - 1);
 
-#ifdef GDN_CTE_PROFILE
-  if (tid == 0 && p.prof) {
-    for (int i = 0; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
-  }
-#endif
   // final state tile -> HBM (fp32)
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
@@ -1205,10 +1132,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     }
   }
 
-#ifdef GDN_CTE_PROFILE
-  unsigned long long prof_acc[kProfSlots] = {};
-  unsigned long long prof_last = __builtin_readcyclecounter();
-#endif
 
   // ---- mover state: loop-invariant offsets (bytes from the chunk start) and
   //      LDS element offsets of every item, and the in-flight registers
@@ -1356,29 +1279,21 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   // scale Gam Q H while the compute waves run B (H of chunk c is in LDS
   // then), + P U once U is there.
   auto mover_chunk = [&](Regs& m, int c) {
-    PROF_MARK_AT(8, kThreads)
     st_k(m, (c + 1) & 1);
     ld_k(m, c + 3);
-    PROF_MARK_AT(15, kThreads)
     flush_out(c - 1);
     f4 oacc[NVB];
     out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]), m.Qf);
     ld_q(m, c + 2);
-    PROF_MARK_AT(9, kThreads)
     __syncthreads();  // end of B
-    PROF_MARK_AT(10, kThreads)
     st_vg(m);
     ld_vg(m, c + 3);
-    PROF_MARK_AT(11, kThreads)
     __syncthreads();  // end of C
-    PROF_MARK_AT(12, kThreads)
     st_tp(sT, m.T);
     ld_t(m, c + 3);
     out_pu(oacc, m.Pf);
     ld_p(m, c + 2);
-    PROF_MARK_AT(13, kThreads)
     __syncthreads();  // end of D
-    PROF_MARK_AT(14, kThreads)
   };
 
   if (mover) {
@@ -1402,12 +1317,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       mover_chunk(rs1, c + 1);
     }
     flush_out(c_begin + ((c_end - c_begin + 1) & ~1) - 1);
-#ifdef GDN_CTE_PROFILE
-    if (tid == kThreads && p.prof) {
-      for (int i = 8; i < kProfSlots; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
-    p.prof[(size_t)blockIdx.x * kProfSlots + 6] = prof_acc[6];
-    }
-#endif
     return;
   }
 
@@ -1444,9 +1353,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
         store4<T>(sXt + (16 * vb + lr) * LDC + 16 * w + 4 * lg, x[0], x[1], x[2], x[3]);
       }
     }
-    PROF_MARK(1)
     __syncthreads();
-    PROF_MARK(2)
 
     // ------------------------------------------------------------------- C
     // U = T X -> LDS as is and scaled by d_t
@@ -1462,9 +1369,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       store4<T>(sUt + off, u[0], u[1], u[2], u[3]);
       store4<T>(sUd + off, dt[0] * u[0], dt[1] * u[1], dt[2] * u[2], dt[3] * u[3]);
     }
-    PROF_MARK(3)
     __syncthreads();
-    PROF_MARK(4)
 
     // ------------------------------------------------------------------- D
     // H' = Gam_C H + K^T (d U)
@@ -1480,9 +1385,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       hacc[j] = hc;
       store4<T>(sHt + (16 * vb + lr) * LDK + 16 * kb + 4 * lg, hc[0], hc[1], hc[2], hc[3]);
     }
-    PROF_MARK(0)
     __syncthreads();
-    PROF_MARK(5)
   };
   for (int c = c_begin; c < c_end; c += 2) {
     compute_chunk(c);
@@ -1490,11 +1393,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   }
 
 
-#ifdef GDN_CTE_PROFILE
-  if (tid == 0 && p.prof) {
-    for (int i = 0; i < 8; ++i) p.prof[(size_t)blockIdx.x * kProfSlots + i] = prof_acc[i];
-  }
-#endif
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
@@ -1548,11 +1446,7 @@ hipError_t launch_local(const CteParams& p, hipStream_t stream) {
 template <typename T, int DK, int DVT>
 hipError_t launch_state(const CteParams& p, hipStream_t stream) {
   const long grid2 = (long)p.B * p.Hv * ((p.Dv + DVT - 1) / DVT);
-#ifndef GDN_CTE_MOVER_WAVES
   constexpr int MW = 4;
-#else
-  constexpr int MW = GDN_CTE_MOVER_WAVES;
-#endif
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((cte_state_ws_kernel<DK, DVT, MW>), dim3((unsigned)grid2), dim3((kWaves + MW) * kWave), 0,
                        stream, p);
@@ -1576,9 +1470,6 @@ constexpr long kCUs = 256;
 
 // widest state tile that still gives every CU a workgroup
 int pick_dvt(const CteParams& p, int max_dvt) {
-#ifdef GDN_CTE_FORCE_DVT
-  return GDN_CTE_FORCE_DVT;
-#endif
   const long heads = (long)p.B * p.Hv;
   int dvt = 16;
   for (int cand = max_dvt; cand >= 16; cand /= 2) {

@@ -54,9 +54,6 @@ struct CteParams {
   // scratch: per (batch * value head, chunk of 64 tokens) the inverse T and
   // the decayed Q K^T block P, each [64][64] in the compute type
   void* ws;
-  // per-workgroup phase cycle counts, written only by builds compiled with
-  // GDN_CTE_PROFILE (a development aid); NULL otherwise
-  unsigned long long* prof;
   // The decode step's prologue folded into the chunk-local kernel (bf16
   // only; NULL q_raw = off).  That kernel then reads raw q_raw, k_raw (the
   // layout of q, k), writes each row made unit length, x / sqrt(sum x^2 +

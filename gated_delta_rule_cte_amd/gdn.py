@@ -100,17 +100,40 @@ def _dtype_code(t):
 
 
 def _req(t, name, dtype=None, shape=None):
+    """Type, dtype, shape and contiguity of one argument (the device is checked
+    separately by _on_gpu, after every argument's shape)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_gpu(named):
+    """Every tensor on the same GPU device; returns that device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+    return dev
+
+
+def _workspace(t, name="workspace"):
+    import torch
+    _req(t, name, torch.uint8)
+    if t.dim() != 1:
+        raise ValueError(f"{name} must be one-dimensional (bytes)")
     return t
 
 
@@ -130,17 +153,16 @@ def gdn_cte(query, key, value, g_log, beta, scale=1.0, recurrent_state=None,
     _req(value, "value", query.dtype, (B, Hv, S, Dv))
     _req(g_log, "g_log", torch.float32, (B, Hv, S))
     _req(beta, "beta", torch.float32, (B, Hv, S))
-    dev = query.device
     has_init = recurrent_state is not None
     if has_init:
         _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
-        state = recurrent_state
-    else:
-        state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+    if out is not None:
+        _req(out, "out", query.dtype, (B, Hv, S, Dv))
+    dev = _on_gpu([("query", query), ("key", key), ("value", value), ("g_log", g_log), ("beta", beta),
+                   ("recurrent_state", recurrent_state), ("out", out)])
+    state = recurrent_state if has_init else torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((B, Hv, S, Dv), dtype=query.dtype, device=dev)
-    else:
-        _req(out, "out", query.dtype, (B, Hv, S, Dv))
     dt = _dtype_code(query)
     ws_bytes = lib.gdn_cte_workspace_size(B, Hk, Hv, S, Dk, Dv, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -171,17 +193,17 @@ def gdn_cte_fused(q, k, v, b, a, A_log, dt_bias, z, norm_weight, recurrent_state
     _req(A_log, "A_log", torch.float32, (Hv,))
     _req(dt_bias, "dt_bias", torch.float32, (Hv,))
     _req(norm_weight, "norm_weight", torch.float32, (Dv,))
-    dev = q.device
     has_init = recurrent_state is not None
     if has_init:
         _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
-        state = recurrent_state
-    else:
-        state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+    if out is not None:
+        _req(out, "out", q.dtype, (B, Hv, S, Dv))
+    dev = _on_gpu([("q", q), ("k", k), ("v", v), ("z", z), ("b", b), ("a", a), ("A_log", A_log),
+                   ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("recurrent_state", recurrent_state),
+                   ("out", out)])
+    state = recurrent_state if has_init else torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((B, Hv, S, Dv), dtype=q.dtype, device=dev)
-    else:
-        _req(out, "out", q.dtype, (B, Hv, S, Dv))
     dt = _dtype_code(q)
     ws_bytes = lib.gdn_cte_fused_workspace_size(B, Hk, Hv, S, Dk, Dv, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -224,11 +246,18 @@ def gdn_block_cte(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_st
     _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
     if value_dim != Hv * Dv or key_dim * 2 + value_dim != conv_dim or Hk * Dk != key_dim:
         raise ValueError("inconsistent block shapes")
-    dev = hidden.device
+    if out is not None:
+        _req(out, "out", bf, (B, S, value_dim))
+    if conv_state_out is not None:
+        _req(conv_state_out, "conv_state_out", bf, (B, conv_dim, K_win))
+    if recurrent_state_out is not None:
+        _req(recurrent_state_out, "recurrent_state_out", torch.float32, (B, Hv, Dk, Dv))
+    dev = _on_gpu([("hidden", hidden), ("W_in_qkv", W_in_qkv), ("W_in_z", W_in_z), ("W_in_a", W_in_a),
+                   ("W_in_b", W_in_b), ("conv_weight", conv_weight), ("conv_state", conv_state), ("A_log", A_log),
+                   ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("recurrent_state", recurrent_state),
+                   ("out", out), ("conv_state_out", conv_state_out), ("recurrent_state_out", recurrent_state_out)])
     if out is None:
         out = torch.empty((B, S, value_dim), dtype=bf, device=dev)
-    else:
-        _req(out, "out", bf, (B, S, value_dim))
     if conv_state_out is None:
         conv_state_out = torch.empty_like(conv_state)
     if recurrent_state_out is None:
@@ -259,15 +288,17 @@ def gdn_tkg(q, k, v, b, a, A_log, dt_bias, z, norm_weight, state_in,
                          ("dt_bias", dt_bias, (Hv,)), ("norm_weight", norm_weight, (V,)),
                          ("state_in", state_in, (BH, K, V))):
         _req(t, name, torch.float32, shp)
-    dev = q.device
+    if state_out is not None:
+        _req(state_out, "state_out", torch.float32, (BH, K, V))
+    if out is not None:
+        _req(out, "out", torch.bfloat16, (BH, V))
+    dev = _on_gpu([("q", q), ("k", k), ("v", v), ("z", z), ("b", b), ("a", a), ("A_log", A_log),
+                   ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("state_in", state_in),
+                   ("state_out", state_out), ("out", out)])
     if state_out is None:
         state_out = torch.empty_like(state_in)
-    else:
-        _req(state_out, "state_out", torch.float32, (BH, K, V))
     if out is None:
         out = torch.empty((BH, V), dtype=torch.bfloat16, device=dev)
-    else:
-        _req(out, "out", torch.bfloat16, (BH, V))
     _check(lib.gdn_tkg(_ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias),
                        _ptr(z), _ptr(norm_weight), _ptr(state_in), _ptr(state_out), _ptr(out),
                        BH, Hv, K, V, _dtype_code(q), float(rms_eps), _stream(dev)))
@@ -312,7 +343,19 @@ def gdn_block_tkg(hidden, W_in_qkv, W_in_z, W_in_a, W_in_b, conv_weight, conv_st
     _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
     if value_dim != Hv * Dv or key_dim * 2 + value_dim != conv_dim or Hk * Dk != key_dim:
         raise ValueError("inconsistent block shapes")
-    dev = hidden.device
+    if out is not None:
+        _req(out, "out", bf, (B, 1, value_dim))
+    if conv_state_out is not None:
+        _req(conv_state_out, "conv_state_out", bf, (B, conv_dim, K_win))
+    if recurrent_state_out is not None:
+        _req(recurrent_state_out, "recurrent_state_out", torch.float32, (B, Hv, Dk, Dv))
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _on_gpu([("hidden", hidden), ("W_in_qkv", W_in_qkv), ("W_in_z", W_in_z), ("W_in_a", W_in_a),
+                   ("W_in_b", W_in_b), ("conv_weight", conv_weight), ("conv_state", conv_state), ("A_log", A_log),
+                   ("dt_bias", dt_bias), ("norm_weight", norm_weight), ("recurrent_state", recurrent_state),
+                   ("out", out), ("conv_state_out", conv_state_out), ("recurrent_state_out", recurrent_state_out),
+                   ("workspace", workspace)])
     if conv_state_out is None:
         conv_state_out = torch.empty_like(conv_state)
     if recurrent_state_out is None:

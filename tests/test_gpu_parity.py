@@ -241,20 +241,19 @@ def test_cte_gqa_s4096_workload(gpu_lib):
 
 
 def test_cte_long_batched_workload_and_chaining(gpu_lib):
-    """B=4, Hk=16, Hv=32, S=16384, D=128, bf16, zero state: sampled heads against
-    the oracle; four chained S=4096 calls carrying the state equal the single call."""
+    """B=4, Hk=16, Hv=32, S=16384, D=128, bf16, zero state: all 128 (batch, value
+    head) slices of the output and the final state against the oracle; four
+    chained S=4096 calls carrying the state equal the single call bit for bit."""
     import torch
     d = inputs.workload_inputs("cte_bf16_b4_hk16_hv32_s16384_d128")
     q, k, v = dev(d["query"]), dev(d["key"]), dev(d["value"])
     g, be = dev(d["g_log"]), dev(d["beta"])
     out, st = gpu_lib.gdn_cte(q, k, v, g, be, d["scale"])
     _sync()
-    heads = [(0, 0), (1, 7), (2, 16), (3, 31), (3, 1), (0, 30)]
-    ref = _oracle_cte(d, False, heads)
-    o_h, s_h = host(out), host(st)
-    for (b, h), (ro, rs) in ref.items():
-        assert_close(o_h[b:b + 1, h:h + 1], ro, TOL_BF16, 2, f"out head {(b, h)}")
-        assert_close(s_h[b:b + 1, h:h + 1], rs, TOL_BF16, 2, f"state head {(b, h)}")
+    ro, rs = _oracle_cte(d, False)
+    assert_close(host(out), ro, TOL_BF16, 2, "out")
+    assert_close(host(st), rs, TOL_BF16, 2, "state")
+    del ro, rs
     # chained: 4 x 4096 with the state carried
     state = None
     outs = []
@@ -307,15 +306,97 @@ def test_cte_is_deterministic(gpu_lib):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_cte_special_cases_on_gpu(gpu_lib):
-    """beta = 0 is pure decay: state = exp(sum g) S0 exactly up to fp32 rounding."""
-    import torch
-    d = inputs.cte_inputs(1, 1, 2, 256, 64, 64, dtype="f32", state_std=0.05, seed=78)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cte_beta_zero_is_pure_decay(gpu_lib, dt):
+    """beta = 0: nothing is written, so S_t = exp(gam_t) S0 and
+    o_t = scale exp(gam_t) S0^T q_t (gam = inclusive cumsum of g_log), for the
+    outputs of every token and the final state."""
+    d = inputs.cte_inputs(1, 2, 4, 300, 128, 128 if dt == "bf16" else 64, dtype=dt, state_std=0.05, seed=78)
     d["beta"] = inputs.f32(np.zeros_like(d["beta"].data))
     o, s = _run_cte(gpu_lib, d, True)
-    gam = np.cumsum(d["g_log"].f64(), axis=-1)
-    ref_s = np.exp(gam[..., -1])[..., None, None] * d["recurrent_state"].f64()
-    assert_close(s, ref_s, TOL_F32, 2, "pure-decay state")
+    gam = np.cumsum(d["g_log"].f64(), axis=-1)                       # [B, Hv, S]
+    S0 = d["recurrent_state"].f64()                                  # [B, Hv, Dk, Dv]
+    G = d["value"].shape[1] // d["query"].shape[1]
+    qv = np.repeat(d["query"].f64(), G, axis=1)                      # [B, Hv, S, Dk]
+    ref_o = d["scale"] * np.exp(gam)[..., None] * np.einsum("bhsk,bhkv->bhsv", qv, S0)
+    ref_s = np.exp(gam[..., -1])[..., None, None] * S0
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(o, ref_o, tol, 2, "pure-decay outputs")
+    assert_close(s, ref_s, tol, 2, "pure-decay state")
+
+
+def _orthonormal_keys_case(dtype, n, Dk, Dv, seed):
+    """g = 0, beta = 1, q_t = k_t, keys k_0..k_{n-1} orthonormal: fp32 keys
+    are rows of a random orthogonal matrix; bf16 keys are signed unit
+    vectors (exact in bf16)."""
+    rng = np.random.default_rng(seed)
+    if dtype == "f32":
+        Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+        keys = Qm[:n]
+    else:
+        keys = np.zeros((n, Dk))
+        keys[np.arange(n), rng.permutation(Dk)[:n]] = rng.choice([-1.0, 1.0], n)
+    d = inputs.cte_inputs(1, 1, 1, n, Dk, Dv, dtype=dtype, state_std=0.05, seed=seed)
+    kq = inputs.cast(keys[None, None], dtype)
+    d["query"], d["key"] = kq, kq
+    d["g_log"] = inputs.f32(np.zeros((1, 1, n)))
+    d["beta"] = inputs.f32(np.ones((1, 1, n)))
+    return d, keys
+
+
+@pytest.mark.parametrize("dt,n", [("f32", 100), ("bf16", 100), ("bf16", 128)])
+def test_cte_write_exact_with_orthonormal_keys(gpu_lib, dt, n):
+    """With g = 0 and beta = 1 the rule writes v exactly: after the call
+    S^T k_j = v_j for every written key, o_t = scale v_t (q_t = k_t), and
+    directions orthogonal to every written key keep S0's response."""
+    Dk, Dv = 128, 64 if dt == "f32" else 128
+    d, keys = _orthonormal_keys_case(dt, n, Dk, Dv, seed=80 + n)
+    o, s = _run_cte(gpu_lib, d, True)
+    kf = d["key"].f64()[0, 0]                                        # the keys the device read
+    v = d["value"].f64()[0, 0]
+    S0 = d["recurrent_state"].f64()[0, 0]
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(o[0, 0], d["scale"] * v, tol, 0, "outputs = scale v")
+    assert_close(kf @ s[0, 0], v, tol, 0, "S^T k_j = v_j")
+    if n < Dk:
+        # an orthonormal basis of the complement of the written keys
+        u = np.linalg.svd(kf, full_matrices=True)[2][n:]
+        assert_close(u @ s[0, 0], u @ S0, tol, 0, "orthogonal directions keep S0")
+
+
+def test_cte_zero_state_never_reads_the_buffer(gpu_lib):
+    """has_initial_state = 0 through the C ABI with the state buffer filled with
+    NaN: the state is never read (the outputs and final state are finite and
+    equal, bit for bit, those of a call whose buffer holds zeros)."""
+    import ctypes
+    import torch
+    for dt, Dk in (("bf16", 128), ("f32", 64)):
+        d = inputs.cte_inputs(1, 2, 4, 333, Dk, Dk, dtype=dt, seed=79)
+        q, k, v, g, be = (dev(d[n]) for n in ("query", "key", "value", "g_log", "beta"))
+        B, Hk, S, _ = q.shape
+        Hv = v.shape[1]
+        lib = gpu_lib.load()
+        code = gpu_lib.GDN_BF16 if dt == "bf16" else gpu_lib.GDN_F32
+        ws_bytes = lib.gdn_cte_workspace_size(B, Hk, Hv, S, Dk, Dk, code)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        res = []
+        for fill in (float("nan"), 0.0):
+            st = torch.full((B, Hv, Dk, Dk), fill, dtype=torch.float32, device=q.device)
+            out = torch.empty_like(v)
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            rc = lib.gdn_cte(*(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, g, be)), d["scale"],
+                             ctypes.c_void_p(st.data_ptr()), 0, ctypes.c_void_p(out.data_ptr()),
+                             B, Hk, Hv, S, Dk, Dk, code, 0, ctypes.c_void_p(ws.data_ptr()), ws_bytes, stream)
+            assert rc == 0, lib.gdn_last_error().decode()
+            _sync()
+            res.append((out, st))
+        (o1, s1), (o0, s0) = res
+        assert torch.isfinite(o1.float()).all() and torch.isfinite(s1).all(), f"{dt}: the NaN buffer was read"
+        assert torch.equal(o1, o0) and torch.equal(s1, s0), f"{dt}: result depends on the unused buffer"
+        ro, rs = _oracle_cte(d, False)
+        tol = TOL_F32 if dt == "f32" else TOL_BF16
+        assert_close(host(o1), ro, tol, 2, f"{dt} out")
+        assert_close(host(s1), rs, tol, 2, f"{dt} state")
 
 
 # ---------------------------------------------------------------------------
@@ -456,16 +537,10 @@ def test_block_b64_workload_in_place(gpu_lib):
 # ---------------------------------------------------------------------------
 # the fused prefill and the prefill layer at the shapes bench.py times
 # ---------------------------------------------------------------------------
-# Value heads are independent: head h needs only key head h // (Hv/Hk), its own
-# v, z, b, a, gate parameters and state (and, in the layer, the in_proj columns
-# and conv channels of those).  So the oracle runs on one-head sub-problems
-# gathered for a few sampled heads, while the GPU runs the whole shape once.
-SAMPLED_HEADS = (0, 17, 31)
-
-
-def test_cte_fused_bench_shape_sampled_heads(gpu_lib):
+def test_cte_fused_bench_shape_all_heads(gpu_lib):
     """gdn_cte_fused at B=1, Hk=16, Hv=32, S=4096, D=128, bf16, supplied state
-    (the bench's fused-prefill call and seed): sampled heads against the oracle."""
+    (the bench's fused-prefill call and seed): every value head's output and
+    state against the oracle."""
     B, Hk, Hv, S, D = 1, 16, 32, 4096, 128
     d = inputs.cte_fused_inputs(B, Hk, Hv, S, D, D, dtype="bf16", state_std=0.05, seed=11)
     st = dev(d["recurrent_state"]).clone()
@@ -473,23 +548,29 @@ def test_cte_fused_bench_shape_sampled_heads(gpu_lib):
                                      dev(d["A_log"]), dev(d["dt_bias"]), dev(d["z"]), dev(d["norm_weight"]),
                                      recurrent_state=st)
     _sync()
-    y, state = host(y), host(state)
-    G = Hv // Hk
-    for h in SAMPLED_HEADS:
-        hk, sl = h // G, slice(h, h + 1)
-        ry, rs = gdn_ref.cte_fused(d["q"].f64()[:, hk:hk + 1], d["k"].f64()[:, hk:hk + 1], d["v"].f64()[:, sl],
-                                   d["b"].f64()[:, sl], d["a"].f64()[:, sl], d["A_log"].f64()[sl],
-                                   d["dt_bias"].f64()[sl], d["z"].f64()[:, sl], d["norm_weight"].f64(),
-                                   d["recurrent_state"].f64()[:, sl])
-        assert_close(y[:, sl], ry, TOL_BF16, 2, f"out, head {h}")
-        assert_close(state[:, sl], rs, TOL_BF16, 2, f"state, head {h}")
+    ry, rs = _oracle_cte_fused(d, d["recurrent_state"].f64())
+    assert_close(host(y), ry, TOL_BF16, 2, "out")
+    assert_close(host(state), rs, TOL_BF16, 2, "state")
 
 
-def test_block_cte_bench_shape_sampled_heads(gpu_lib):
+def _oracle_cte_fused(d, s0):
+    """oracle.gdn_ref.cte_fused with its recurrence on the C twin (the same
+    token-by-token definition, OpenMP over heads), for the bench shapes."""
+    Dk = d["q"].shape[-1]
+    q_unit, k_unit = gdn_ref.l2norm(d["q"].f64()), gdn_ref.l2norm(d["k"].f64())
+    beta = gdn_ref.sigmoid(d["b"].f64())
+    rate = np.exp(d["A_log"].f64())[None, :, None]
+    g = -rate * gdn_ref.softplus(d["a"].f64() + d["dt_bias"].f64()[None, :, None])
+    O, S1 = c_ref.cte(q_unit, k_unit, d["v"].f64(), g, beta, 1.0 / math.sqrt(Dk), s0)
+    return gdn_ref.rms_norm_gated(O, d["z"].f64(), d["norm_weight"].f64()), S1
+
+
+def test_block_cte_bench_shape_all_heads(gpu_lib):
     """gdn_block_cte at B=1, S=4096, H=2048, Hk=16, Hv=32, D=128, K_win=4 with the
-    caches updated in place (the bench's prefill-layer call and seed): sampled
-    heads of the output and the recurrent state against one-head oracle layers,
-    and the whole final conv window against the oracle's last K_win projections."""
+    caches updated in place (the bench's prefill-layer call and seed): every
+    value head of the output and the recurrent state against the oracle's
+    layer, and the final conv window against the oracle's last K_win
+    projections."""
     B, S, H, Hk, Hv, D, Kw = 1, 4096, 2048, 16, 32, 128, 4
     d = inputs.block_cte_inputs(B, S, H, Hk, Hv, D, D, K_win=Kw, seed=12)
     cs = dev(d["conv_state"]).clone()
@@ -501,27 +582,36 @@ def test_block_cte_bench_shape_sampled_heads(gpu_lib):
     out, cs1, rs1 = host(out), host(cs1), host(rs1)
     f = {n: d[n].f64() for n in ("hidden", "W_in_qkv", "W_in_z", "W_in_a", "W_in_b", "conv_weight", "conv_state",
                                  "A_log", "dt_bias", "norm_weight", "recurrent_state")}
+    # the oracle layer (gdn_ref.block_cte) with its recurrence on the C twin
     key_dim = Hk * D
-    G = Hv // Hk
-    for h in (0, 31):  # first and second value head of a GQA pair, first and last key head
-        hk = h // G
-        chans = np.r_[hk * D:(hk + 1) * D, key_dim + hk * D:key_dim + (hk + 1) * D,
-                      2 * key_dim + h * D:2 * key_dim + (h + 1) * D]
-        sl = slice(h, h + 1)
-        ry, rcs, rrs = gdn_ref.block_cte(f["hidden"], f["W_in_qkv"][:, chans], f["W_in_z"][:, h * D:(h + 1) * D],
-                                         f["W_in_a"][:, sl], f["W_in_b"][:, sl], f["conv_weight"][chans],
-                                         f["conv_state"][:, chans], f["A_log"][sl], f["dt_bias"][sl],
-                                         f["norm_weight"], f["recurrent_state"][:, sl], 1, 1, D, D)
-        assert_close(out[:, :, h * D:(h + 1) * D], ry, TOL_BF16, 1, f"out, head {h}")
-        assert_close(rs1[:, sl], rrs, TOL_BF16, 2, f"recurrent state, head {h}")
-        assert_bf16_sums_match(cs1[:, chans], rcs, f["hidden"][:, -Kw:], f["W_in_qkv"][:, chans],
-                               f"conv window, head {h}")
-    # the final window holds the last K_win conv inputs of every channel: the
-    # oracle layer over the last K_win tokens (the old window shifts out) gives it
-    _, rcs_all, _ = gdn_ref.block_cte(f["hidden"][:, -Kw:], f["W_in_qkv"], f["W_in_z"], f["W_in_a"], f["W_in_b"],
-                                      f["conv_weight"], f["conv_state"], f["A_log"], f["dt_bias"],
-                                      f["norm_weight"], f["recurrent_state"], Hk, Hv, D, D)
-    assert_bf16_sums_match(cs1, rcs_all, f["hidden"][:, -Kw:], f["W_in_qkv"], "conv window")
+    x = f["hidden"].reshape(B * S, H)
+    mixed = gdn_ref.in_proj(x, f["W_in_qkv"]).reshape(B, S, -1)
+    zz = gdn_ref.in_proj(x, f["W_in_z"]).reshape(B, S, Hv, D).transpose(0, 2, 1, 3)
+    aa = gdn_ref.in_proj(x, f["W_in_a"]).reshape(B, S, Hv).transpose(0, 2, 1)
+    bb = gdn_ref.in_proj(x, f["W_in_b"]).reshape(B, S, Hv).transpose(0, 2, 1)
+    conv_out, window = gdn_ref.conv1d_prefill(mixed, f["conv_state"], f["conv_weight"])
+    conv_out = gdn_ref.bf16_round(conv_out)
+    q = conv_out[:, :, :key_dim].reshape(B, S, Hk, D).transpose(0, 2, 1, 3)
+    k = conv_out[:, :, key_dim:2 * key_dim].reshape(B, S, Hk, D).transpose(0, 2, 1, 3)
+    v = conv_out[:, :, 2 * key_dim:].reshape(B, S, Hv, D).transpose(0, 2, 1, 3)
+    sub = {n: _F64(a) for n, a in (("q", q), ("k", k), ("v", v), ("b", bb), ("a", aa), ("A_log", f["A_log"]),
+                                   ("dt_bias", f["dt_bias"]), ("z", zz), ("norm_weight", f["norm_weight"]))}
+    ry, rrs = _oracle_cte_fused(sub, f["recurrent_state"])
+    ry = ry.transpose(0, 2, 1, 3).reshape(B, S, Hv * D)
+    assert_close(out.reshape(B * S, Hv, D).transpose(1, 0, 2), ry.reshape(B * S, Hv, D).transpose(1, 0, 2),
+                 TOL_BF16, 1, "out (per value head)")
+    assert_close(rs1, rrs, TOL_BF16, 2, "recurrent state")
+    assert_bf16_sums_match(cs1, window, f["hidden"][:, -Kw:], f["W_in_qkv"], "conv window")
+
+
+class _F64:
+    """A float64 array in the place of an inputs.Arr (its .f64() and .shape)."""
+    def __init__(self, a):
+        self.a = np.asarray(a, np.float64)
+        self.shape = self.a.shape
+
+    def f64(self):
+        return self.a
 
 
 def assert_bf16_sums_match(x, ref, hidden, W, what, max_frac=1e-2):
