@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_tkg.hip", "gdn_cte.hip", "gdn_block.hip", "gdn_fused.hip", "gdn_block_cte.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_tkg.hip", "gdn_cte.hip", "gdn_block.hip", "gdn_fused.hip", "gdn_block_cte.hip",
+           "gdn_noalloc.hip"]
 # measurement aids for bench.py, in a library of their own
 CALIB_LIB = os.path.join(PKG, "libgdn_calib.so")
 CALIB_SOURCES = ["gdn_calib.hip"]

@@ -107,6 +107,18 @@ size_t esize(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
 
 }  // namespace
 
+namespace gdn {
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+}  // namespace gdn
+
 extern "C" {
 
 int gdn_version(void) { return 100; }

@@ -8,6 +8,9 @@
 
 namespace gdn {
 
+// records a message for gdn_last_error() (printf format) and returns `code`
+int set_error(int code, const char* fmt, ...);
+
 // ---------------------------------------------------------------- decode step
 struct TkgParams {
   // q/k row of head bh = b * Hv + h starts at base + b * qk_bstride + (h / head_div) * K

@@ -25,7 +25,7 @@ STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_DTY
           -7: "GDN_ERR_UNSUPPORTED", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_DEVICE"}
 
 #: every symbol include/gdn.h declares
-EXPORTS = ("gdn_cte", "gdn_cte_workspace_size", "gdn_cte_fused", "gdn_cte_fused_workspace_size",
+EXPORTS = ("gdn_cte", "gdn_cte_workspace_size", "gdn_cte_noalloc", "gdn_cte_fused", "gdn_cte_fused_workspace_size",
            "gdn_block_cte", "gdn_block_cte_workspace_size", "gdn_tkg", "gdn_block_tkg",
            "gdn_block_tkg_workspace_size", "gdn_status_string", "gdn_last_error",
            "gdn_version")
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_cte.restype = I
     lib.gdn_cte_workspace_size.argtypes = [I] * 7
     lib.gdn_cte_workspace_size.restype = Z
+    lib.gdn_cte_noalloc.argtypes = [P, P, P, P, P, F, P, I, P, I, I, I, I, I, I, I, I, P]
+    lib.gdn_cte_noalloc.restype = I
     lib.gdn_cte_fused.argtypes = [P] * 10 + [I, P] + [I] * 8 + [F, P, Z, P]
     lib.gdn_cte_fused.restype = I
     lib.gdn_cte_fused_workspace_size.argtypes = [I] * 7
@@ -171,6 +173,31 @@ def gdn_cte(query, key, value, g_log, beta, scale=1.0, recurrent_state=None,
                        B, Hk, Hv, S, Dk, Dv, dt, int(algorithm), _ptr(ws), ws_bytes,
                        _stream(dev)))
     return out, state
+
+
+def gdn_cte_noalloc(query, key, value, g_log, beta, scale, recurrent_state, out,
+                    has_initial_state=True, algorithm=GDN_CTE_ALGO_DEFAULT):
+    """gdn_cte on the library's fixed scratch (no device allocation anywhere:
+    the caller passes every output).  ``recurrent_state`` [B,Hv,Dk,Dv] fp32 is
+    read as the initial state when ``has_initial_state`` and receives the
+    final state; ``out`` [B,Hv,S,Dv].  Returns (out, recurrent_state)."""
+    import torch
+    lib = load()
+    B, Hk, S, Dk = query.shape
+    Hv, Dv = value.shape[1], value.shape[3]
+    _req(query, "query")
+    _req(key, "key", query.dtype, (B, Hk, S, Dk))
+    _req(value, "value", query.dtype, (B, Hv, S, Dv))
+    _req(g_log, "g_log", torch.float32, (B, Hv, S))
+    _req(beta, "beta", torch.float32, (B, Hv, S))
+    _req(recurrent_state, "recurrent_state", torch.float32, (B, Hv, Dk, Dv))
+    _req(out, "out", query.dtype, (B, Hv, S, Dv))
+    dev = _on_gpu([("query", query), ("key", key), ("value", value), ("g_log", g_log), ("beta", beta),
+                   ("recurrent_state", recurrent_state), ("out", out)])
+    _check(lib.gdn_cte_noalloc(_ptr(query), _ptr(key), _ptr(value), _ptr(g_log), _ptr(beta), float(scale),
+                               _ptr(recurrent_state), int(bool(has_initial_state)), _ptr(out),
+                               B, Hk, Hv, S, Dk, Dv, _dtype_code(query), int(algorithm), _stream(dev)))
+    return out, recurrent_state
 
 
 def gdn_cte_fused(q, k, v, b, a, A_log, dt_bias, z, norm_weight, recurrent_state=None,

@@ -115,6 +115,32 @@ int gdn_cte(const void* query, const void* key, const void* value,
 size_t gdn_cte_workspace_size(int B, int Hk, int Hv, int S, int Dk, int Dv,
                               int dtype);
 
+/* Bytes of the fixed device scratch gdn_cte_noalloc uses (per GPU). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * gdn_cte_noalloc - gdn_cte for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The arguments, results and checks are gdn_cte's; the workspace
+ * is instead a fixed array of GDN_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends.  Nothing is allocated or freed.
+ *   - A call whose gdn_cte_workspace_size() exceeds that size returns
+ *     GDN_ERR_WORKSPACE (nothing launched); gdn_cte with a caller-owned
+ *     workspace has no such limit.
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, or host threads racing to one
+ *     stream's queue) race on it and give wrong results.  The array needs no
+ *     clearing: each call writes every byte it later reads.
+ *   - All of gdn_cte's argument checks run before the first HIP call; on its
+ *     first call on a device the entry point then looks up the array's
+ *     address on that device (GDN_ERR_DEVICE if it cannot).
+ */
+int gdn_cte_noalloc(const void* query, const void* key, const void* value,
+                    const float* g_log, const float* beta, float scale,
+                    float* recurrent_state, int has_initial_state, void* out,
+                    int B, int Hk, int Hv, int S, int Dk, int Dv, int dtype,
+                    int algorithm, void* stream);
+
 /*
  * gdn_cte_fused - chunked prefill with the decode step's gates and output norm.
  * The steps either side of gdn_cte: "GDN CTE Kernel API Reference", gdn_cte
