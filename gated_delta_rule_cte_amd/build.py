@@ -43,6 +43,18 @@ def compile_flags(extra=()):
             "-I", INCLUDE, "-I", CSRC, *extra]
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources: only the host code (argument validation, dispatch) is instrumented
+# (each flag behind -Xarch_host); the GPU code is built as usual.  The
+# sanitizer runtime is not linked in: the process that loads the library
+# preloads clang's shared ASan runtime (tests/sanitize_host.py does).
+HOSTSAN_LIB = os.path.join(PKG, "libgdn_hostsan.so")
+HOSTSAN_DIR = os.path.join(PKG, "_build_hostsan")
+HOSTSAN_FLAGS = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g")
+
+
 def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
     _link(SOURCES, out, verbose, extra_flags)
     if out == LIB:
@@ -50,12 +62,17 @@ def build(verbose: bool = True, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
-def _link(sources, out, verbose, extra_flags):
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build_host_sanitized(verbose: bool = True) -> str:
+    _link(SOURCES, HOSTSAN_LIB, verbose, HOSTSAN_FLAGS, build_dir=HOSTSAN_DIR)
+    return HOSTSAN_LIB
+
+
+def _link(sources, out, verbose, extra_flags, build_dir=BUILD_DIR):
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
 
     def one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         vg = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] if src in VGPR_MFMA else []
         cmd = [cc, *compile_flags(extra_flags), *vg, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -81,4 +98,7 @@ def _link(sources, out, verbose, extra_flags):
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose="-q" not in sys.argv)
+    else:
+        build(verbose="-q" not in sys.argv)

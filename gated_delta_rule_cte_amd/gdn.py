@@ -15,7 +15,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+# GDN_LIBRARY selects another build of the same library (for instance the
+# host-sanitized one that tests/sanitize_host.py builds)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 GDN_CTE_ALGO_DEFAULT = 0

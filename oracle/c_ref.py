@@ -13,7 +13,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_ref.c")
-_LIB = os.path.join(_HERE, "liboracle_ref.so")
+# GDN_ORACLE_LIBRARY selects another build of gdn_ref.c (for instance the
+# host-sanitized one that tests/sanitize_host.py builds); it is never rebuilt here
+_LIB_ENV = os.environ.get("GDN_ORACLE_LIBRARY")
+_LIB = _LIB_ENV or os.path.join(_HERE, "liboracle_ref.so")
 _lib = None
 
 
@@ -28,7 +31,7 @@ def build(verbose=False):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_ENV and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         lib = ctypes.CDLL(_LIB)
         P = ctypes.POINTER(ctypes.c_double)
