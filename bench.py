@@ -51,14 +51,16 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "gated_delta_rule_cte_amd", "csrc")
 OP_SOURCES = {
     "cte": ["gdn_api.cpp", "gdn_cte.hip", "gdn_device.h", "gdn_launch.h"],
+    "cte_long": ["gdn_api.cpp", "gdn_cte.hip", "gdn_device.h", "gdn_launch.h"],
     "tkg": ["gdn_api.cpp", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
     "block": ["gdn_api.cpp", "gdn_block.hip", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
 }
 # kernels of each entry point in the bench workloads: (name fragment, grid in threads or None)
 OP_KERNELS = {
-    "cte": [("cte_local", None), ("cte_state", None)],
+    "cte": [("cte_local1_kernel<128, 2, 0, false>", 1 * 32 * 64 // 2 * 64), ("cte_state_ws_kernel<128, 16,", None)],
+    "cte_long": [("cte_local1_kernel<128, 2, 0, false>", 4 * 32 * 256 // 2 * 64), ("cte_state_ws_kernel<128, 64,", None)],
     "tkg": [("tkg_kernel", 1024 * 256)],
-    "block": [("block_proj_kernel", None), ("tkg_kernel", 2048 * 256)],
+    "block": [("block_proj", None), ("tkg_kernel", 2048 * 256)],
 }
 COPY_CAL_BYTES = 512 << 20
 
@@ -333,6 +335,29 @@ def compare_inverse(gdn, torch, dev):
         torch.cuda.empty_cache()
     print(json.dumps({"compare_inverse": rows, "config": {"workload": "gdn_cte bf16 B=1 Hk=16 Hv=32 D=128, "
                       "supplied fp32 state, S = 128 ... 16384"}, "timing": "graphs of 8 calls, HIP events"}))
+
+
+LONG = dict(B=4, Hk=16, Hv=32, S=16384, D=128)
+
+
+def long_inputs(gdn, torch, dev):
+    """The long prefill's inputs on the device; returns its single call."""
+    B, Hk, Hv, S, D = (LONG[k] for k in ("B", "Hk", "Hv", "S", "D"))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    q = torch.randn(B, Hk, S, D, device=dev, generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    k = torch.randn(B, Hk, S, D, device=dev, generator=gen)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn(B, Hv, S, D, device=dev, generator=gen).to(torch.bfloat16)
+    g = -(0.005 + 0.295 * torch.rand(B, Hv, S, device=dev, generator=gen))
+    be = 0.05 + 0.9 * torch.rand(B, Hv, S, device=dev, generator=gen)
+    out = torch.empty(B, Hv, S, D, device=dev, dtype=torch.bfloat16)
+
+    def single():
+        gdn.gdn_cte(q, k, v, g, be, D ** -0.5, out=out)
+
+    return single
 
 
 def long_prefill(gdn, torch, dev, reps=5):
@@ -649,7 +674,14 @@ def main():
                 for s in sets:
                     fn(s)
             torch.cuda.synchronize()
-        print(json.dumps({"eager_calls_per_op": args.eager * NSETS + NSETS, "ops": [n for n, _, _ in ops]}))
+        if not args.no_long:  # the long prefill's single call, for its counters
+            long_single = long_inputs(gdn, torch, dev)
+            for _ in range(args.eager + 1):
+                long_single()
+            torch.cuda.synchronize()
+            del long_single
+        print(json.dumps({"eager_calls_per_op": args.eager * NSETS + NSETS, "ops": [n for n, _, _ in ops],
+                          "long_single_calls": 0 if args.no_long else args.eager + 1}))
         return
 
     # -------------------------------------------------------------- graphs
