@@ -433,8 +433,8 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   f.S = S; f.Hv = Hv; f.Dk = Dk;
   gdn::CteParams p{};
   if (gdn::fused_inplace_ok(Hk, Hv)) {
-    // the chunk-local kernel forms the unit rows over the raw ones (one wave
-    // reads and writes each key head's chunk) and the gates
+    // the chunk-local kernel forms the unit rows over the raw ones (one
+    // workgroup reads and writes each key head's chunk) and the gates
     p.q_raw = f.q; p.k_raw = f.k; p.b_raw = f.b; p.a_raw = f.a; p.A_log = A_log; p.dt_bias = dt_bias;
     p.qn = f.qn; p.kn = f.kn; p.g_out = f.g; p.beta_out = f.beta;
   } else if ((e = gdn::launch_fused_pre(f, GDN_BF16, hs)) != hipSuccess) {

@@ -388,24 +388,35 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
   return c;
 }
 
-// NG value heads that share a key head (GQA) per wave: the raw K K^T and
-// Q K^T products are the same for all of them; only beta and the decays differ.
+// One workgroup per (chunk, key head, NG value heads of its GQA group), one
+// wave per value head.  The waves of a workgroup load the same K and Q rows
+// (the second read hits the cache) and form the same raw K K^T and Q K^T;
+// each then applies its own head's beta and decays.  Each wave owns one LDS
+// buffer of packed fp32 blocks that holds A, then T (the diagonal blocks of
+// T replace A's once the substitution has read them, the rest once the
+// levels are done), then P in bf16 for the stores, so two workgroups of two
+// waves fit per SIMD pair and one wave's loads overlap another's inverse.
+// (The Neumann series needs the power and the running product side by side:
+// it keeps a second buffer.)
 // FUSE: the decode step's prologue is folded in (raw q, k and gates in; unit
 // rows of q, k and beta, g out for the state pass), see CteParams.
 template <int DK, int NG, int ALGO, bool FUSE>
-__global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
+__global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
   using MM = Mfma<T>;
   constexpr int C = kC, NB = kNB, NS = DK / 32;
+  constexpr int kBufs = ALGO == kAlgoNeumann ? 2 : 1;
 
-  __shared__ __align__(16) float sA[kNTri * kBlkF];  // A; P (bf16) once the inverse is done
-  __shared__ __align__(16) float sTb[kNTri * kBlkF];
-  __shared__ __align__(16) float sGam[C];
-  __shared__ __align__(16) float sBeta[C];
+  __shared__ __align__(16) float sbuf[NG][kBufs][kNTri * kBlkF];
+  __shared__ __align__(16) float sGamW[NG][C];
+  __shared__ __align__(16) float sBetaW[NG][C];
 
-  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-  const int tid = lane;
+  const int w = threadIdx.x >> 6;  // value head hh0 + w of the group
+  const int lane = threadIdx.x & (kWave - 1), lr = lane & 15, lg = lane >> 4;
+  float* const sA = sbuf[w][0];
+  float* const sGam = sGamW[w];
+  float* const sBeta = sBetaW[w];
   const int S = p.S, Dk = p.Dk, Hk = p.Hk, Hv = p.Hv;
   const int NC = (S + C - 1) / C;
   const int G = Hv / Hk;
@@ -416,7 +427,7 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
   const int c = p.c_begin + (lid / GN) % nseg;
   const int bhk = lid / (GN * nseg);
   const int b = bhk / Hk, hk = bhk - b * Hk;
-  const int bh0 = b * Hv + hk * G + hh0;  // first value head of this wave
+  const int bh = b * Hv + hk * G + hh0 + w;  // this wave's value head
   const int c0 = c * C;
   const uint32_t rem = (uint32_t)(S - c0);
 
@@ -439,7 +450,7 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       kf[rb][s] = V8::bload(rK, off);
       qf[rb][s] = V8::bload(rQ, off);
     }
-  float gln[NG], ben[NG];
+  float gln, ben;
   if constexpr (FUSE) {
     // Each row made unit length: lane (lr, lg) holds 8 columns of row
     // 16 rb + lr in each of its NS fragments, the rest of the row is in lanes
@@ -467,7 +478,11 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       unit_rows(kf[rb]);
       unit_rows(qf[rb]);
     }
-    if (hh0 == 0) {
+    // The unit rows may be written over the raw ones (in place): every wave
+    // of the workgroup has used its raw rows (the loads have returned) before
+    // wave 0 writes.
+    if constexpr (NG > 1) __syncthreads();
+    if (hh0 == 0 && w == 0) {
       const auto wK = make_rsrc(static_cast<T*>(p.kn) + qk0, rem * Dk * 2u);
       const auto wQ = make_rsrc(static_cast<T*>(p.qn) + qk0, rem * Dk * 2u);
 #pragma unroll
@@ -482,25 +497,19 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
     // beta = sigmoid(b), g = -exp(A_log[h]) softplus(a + dt_bias[h]) for the
     // token of this lane; zero past the sequence end
     const bool tv = c0 + lane < S;
-#pragma unroll
-    for (int n = 0; n < NG; ++n) {
-      const size_t row = (size_t)(bh0 + n) * S + c0;
-      const int h = (bh0 + n) % Hv;
-      const float bb = buf_load_f32(make_rsrc(p.b_raw + row, rem * 4u), (uint32_t)lane * 4u);
-      const float aa = buf_load_f32(make_rsrc(p.a_raw + row, rem * 4u), (uint32_t)lane * 4u);
-      gln[n] = tv ? -expf(p.A_log[h]) * softplusf_(aa + p.dt_bias[h]) : 0.f;
-      ben[n] = tv ? sigmoidf_(bb) : 0.f;
-      if (tv) {
-        p.g_out[row + lane] = gln[n];
-        p.beta_out[row + lane] = ben[n];
-      }
+    const size_t row = (size_t)bh * S + c0;
+    const int h = bh % Hv;
+    const float bb = buf_load_f32(make_rsrc(p.b_raw + row, rem * 4u), (uint32_t)lane * 4u);
+    const float aa = buf_load_f32(make_rsrc(p.a_raw + row, rem * 4u), (uint32_t)lane * 4u);
+    gln = tv ? -expf(p.A_log[h]) * softplusf_(aa + p.dt_bias[h]) : 0.f;
+    ben = tv ? sigmoidf_(bb) : 0.f;
+    if (tv) {
+      p.g_out[row + lane] = gln;
+      p.beta_out[row + lane] = ben;
     }
   } else {
-#pragma unroll
-    for (int n = 0; n < NG; ++n) {
-      gln[n] = buf_load_f32(make_rsrc(p.g + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
-      ben[n] = buf_load_f32(make_rsrc(p.beta + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
-    }
+    gln = buf_load_f32(make_rsrc(p.g + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
+    ben = buf_load_f32(make_rsrc(p.beta + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
   }
 
   // raw products of the lower blocks, transposed: lane holds row 16 i + lr,
@@ -521,15 +530,12 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
     }
   const float scale = p.scale;
 
-#pragma unroll
-  for (int n = 0; n < NG; ++n) {
-  const int bh = bh0 + n;
-  if (n > 0) wave_lds_sync();  // the previous head's LDS reads are done
-  sGam[lane] = wave_inclusive_scan_dpp(gln[n]);
-  sBeta[lane] = ben[n];
+  sGam[lane] = wave_inclusive_scan_dpp(gln);
+  sBeta[lane] = ben;
   wave_lds_sync();
 
-  // A (packed, fp32) and P (registers)
+  // A (packed, fp32) and P (registers).  Below the diagonal block every
+  // column precedes every row, so only the diagonal blocks are masked.
   f4 pacc[kNTri];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -545,20 +551,23 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       for (int r = 0; r < 4; ++r) {
         const int sc = 16 * j + 4 * lg + r;
         const float e = __expf(gt - gsv[r]);
-        a[r] = sc < t ? bt * kk[r] * e : 0.f;
-        pacc[tri(i, j)][r] = sc <= t ? scale * qk[r] * e : 0.f;
+        a[r] = (j < i || sc < t) ? bt * kk[r] * e : 0.f;
+        pacc[tri(i, j)][r] = (j < i || sc <= t) ? scale * qk[r] * e : 0.f;
       }
       *reinterpret_cast<float4*>(&sA[tri(i, j) * kBlkF + lr * kLB + 4 * lg]) = make_float4(a[0], a[1], a[2], a[3]);
     }
   }
   wave_lds_sync();
 
+  // T, left in sA (row form) in both branches
   if constexpr (ALGO == kAlgoNeumann) {
     // T = (I - A)(I + A^2)(I + A^4) ... (I + A^32): with Pw the running power
     // (-A)^(2^j), Pw <- Pw Pw and T <- T + T Pw, five times.  Every factor is
     // lower block-triangular, so block (i, j) of a product sums m = j..i.
     // Pw and T live in accumulator form (lane: rows 4 lg + r, column lr) and,
-    // as the first operand of the next products, in row form: Pw in sA, T in sTb.
+    // as the first operand of the next products, in row form: T in sA, Pw in
+    // the second buffer.
+    float* const sPw = sbuf[w][kBufs - 1];
     f4 pw[kNTri], tb[kNTri];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -577,8 +586,8 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[q * kBlkF + (4 * lg + r) * kLB + lr] = src[q][r];
     };
-    put(sA, pw);
-    put(sTb, tb);
+    put(sPw, pw);
+    put(sA, tb);
     wave_lds_sync();
 #pragma unroll 1
     for (int step = 1; step < 6; ++step) {
@@ -590,7 +599,7 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
           f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = j; m <= i; ++m)
-            z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), pw[tri(m, j)], z);
+            z = mfma4_f32(*reinterpret_cast<const float4*>(&sPw[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), pw[tri(m, j)], z);
           np[tri(i, j)] = z;
         }
 #pragma unroll
@@ -600,21 +609,22 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
           f4 z = tb[tri(i, j)];
 #pragma unroll
           for (int m = j; m <= i; ++m)
-            z = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), np[tri(m, j)], z);
+            z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), np[tri(m, j)], z);
           tb[tri(i, j)] = z;
         }
 #pragma unroll
       for (int q = 0; q < kNTri; ++q) pw[q] = np[q];
       wave_lds_sync();
-      put(sA, pw);
-      put(sTb, tb);
+      put(sPw, pw);
+      put(sA, tb);
       wave_lds_sync();
     }
   } else {
-    // diagonal blocks of T: lane = (block, column), forward substitution
+    // diagonal blocks of T: lane = (block, column), forward substitution; T's
+    // diagonal blocks then replace A's, which nothing reads again
     {
       const int blk = lane >> 4, j = lane & 15;
-      const float* Ab = sA + tri(blk, blk) * kBlkF;
+      float* const Ab = sA + tri(blk, blk) * kBlkF;
       float tc[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
@@ -631,18 +641,20 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
         for (int m = 0; m < i; ++m) acc += row[m] * tc[m];
         if (i > j) tc[i] = -acc;
       }
-      float* Tb = sTb + tri(blk, blk) * kBlkF;
+      wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[i * kLB + j] = tc[i];
+      for (int i = 0; i < 16; ++i) Ab[i * kLB + j] = tc[i];
     }
     wave_lds_sync();
 
-    // T blocks in the accumulator layout (lane: rows 4 lg + r, column lr)
+    // off-diagonal blocks level by level, T_ij = -T_ii sum_m A_im T_mj, in
+    // the accumulator layout (lane: rows 4 lg + r, column lr); A_im (m < i)
+    // and T_ii are both in sA now
     f4 tb[kNTri];
 #pragma unroll
     for (int d = 0; d < NB; ++d)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tb[tri(d, d)][r] = sTb[tri(d, d) * kBlkF + (4 * lg + r) * kLB + lr];
+      for (int r = 0; r < 4; ++r) tb[tri(d, d)][r] = sA[tri(d, d) * kBlkF + (4 * lg + r) * kLB + lr];
 #pragma unroll
     for (int d = 1; d < NB; ++d) {
 #pragma unroll
@@ -652,19 +664,47 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
 #pragma unroll
         for (int m = j; m < i; ++m)
           z = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, m) * kBlkF + lr * kLB + 4 * lg]), tb[tri(m, j)], z);
-        const f4 tz = mfma4_f32(*reinterpret_cast<const float4*>(&sTb[tri(i, i) * kBlkF + lr * kLB + 4 * lg]), z,
+        const f4 tz = mfma4_f32(*reinterpret_cast<const float4*>(&sA[tri(i, i) * kBlkF + lr * kLB + 4 * lg]), z,
                                 f4{0.f, 0.f, 0.f, 0.f});
         tb[tri(i, j)] = -tz;
       }
     }
+    wave_lds_sync();  // every read of A's off-diagonal blocks is done
 #pragma unroll
     for (int d = 1; d < NB; ++d)
 #pragma unroll
       for (int j = 0; j + d < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sTb[tri(j + d, j) * kBlkF + (4 * lg + r) * kLB + lr] = tb[tri(j + d, j)][r];
+        for (int r = 0; r < 4; ++r) sA[tri(j + d, j) * kBlkF + (4 * lg + r) * kLB + lr] = tb[tri(j + d, j)][r];
   }
-  // P (bf16) into the A area, which the levels above no longer read
+  wave_lds_sync();
+
+  // lower blocks of T -> workspace in bf16, 16-byte stores (item: block,
+  // row, half); then P through the same buffer
+  T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
+  T* Pg = Tg + C * C;
+  auto item = [&](int q, int& blk, size_t& go, int& row, int& half) {
+    const int it = lane + kWave * q;
+    blk = it / 32;
+    row = (it % 32) / 2;
+    half = it % 2;
+    const int bi = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
+    const int bj = blk - tri(bi, 0);
+    go = (size_t)(16 * bi + row) * C + 16 * bj + 8 * half;
+  };
+#pragma unroll
+  for (int q = 0; q < kNTri * 32 / kWave; ++q) {
+    int blk, row, half;
+    size_t go;
+    item(q, blk, go, row, half);
+    const float* src = sA + blk * kBlkF + row * kLB + 8 * half;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    bf16x8 f;
+    f[0] = f2bf(x0.x); f[1] = f2bf(x0.y); f[2] = f2bf(x0.z); f[3] = f2bf(x0.w);
+    f[4] = f2bf(x1.x); f[5] = f2bf(x1.y); f[6] = f2bf(x1.z); f[7] = f2bf(x1.w);
+    *reinterpret_cast<uint4*>(Tg + go) = __builtin_bit_cast(uint4, f);
+  }
   T* sP = reinterpret_cast<T*>(sA);
   wave_lds_sync();
 #pragma unroll
@@ -674,27 +714,13 @@ __global__ __launch_bounds__(kWave) void cte_local1_kernel(const CteParams p) {
       store4<T>(sP + tri(i, j) * 16 * kPB + lr * kPB + 4 * lg, pacc[tri(i, j)][0], pacc[tri(i, j)][1],
                 pacc[tri(i, j)][2], pacc[tri(i, j)][3]);
   wave_lds_sync();
-
-  // lower blocks of T and P -> workspace, 16-byte stores (item: block, row, half)
-  T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
-  T* Pg = Tg + C * C;
 #pragma unroll
   for (int q = 0; q < kNTri * 32 / kWave; ++q) {
-    const int it = lane + kWave * q;
-    const int blk = it / 32, row = (it % 32) / 2, half = it % 2;
-    const int bi = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
-    const int bj = blk - tri(bi, 0);
-    const float* src = sTb + blk * kBlkF + row * kLB + 8 * half;
-    const float4 x0 = *reinterpret_cast<const float4*>(src);
-    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-    bf16x8 f;
-    f[0] = f2bf(x0.x); f[1] = f2bf(x0.y); f[2] = f2bf(x0.z); f[3] = f2bf(x0.w);
-    f[4] = f2bf(x1.x); f[5] = f2bf(x1.y); f[6] = f2bf(x1.z); f[7] = f2bf(x1.w);
-    const size_t go = (size_t)(16 * bi + row) * C + 16 * bj + 8 * half;
-    *reinterpret_cast<uint4*>(Tg + go) = __builtin_bit_cast(uint4, f);
+    int blk, row, half;
+    size_t go;
+    item(q, blk, go, row, half);
     *reinterpret_cast<uint4*>(Pg + go) = *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
   }
-  }  // value heads
 }
 
 // ===========================================================================
@@ -1407,8 +1433,8 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   }
 }
 
-// one wave per (chunk, key head, pair of value heads) when the GQA group is
-// even, else per (chunk, value head)
+// one workgroup per (chunk, key head, pair of value heads) when the GQA group
+// is even, else per (chunk, value head); one wave per value head
 constexpr int local1_ng(int Hk, int Hv) { return (Hv / Hk) % 2 == 0 ? 2 : 1; }
 
 template <int DK, bool FUSE>
@@ -1416,10 +1442,11 @@ hipError_t launch_local1(const CteParams& p, long grid1, hipStream_t stream) {
   const bool neu = p.algo == kAlgoNeumann;
   if (local1_ng(p.Hk, p.Hv) == 2) {
     if (neu)
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0,
-                         stream, p);
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(2 * kWave),
+                         0, stream, p);
     else
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(kWave), 0, stream, p);
+      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(2 * kWave), 0, stream,
+                         p);
   } else if (neu)
     hipLaunchKernelGGL((cte_local1_kernel<DK, 1, kAlgoNeumann, FUSE>), dim3((unsigned)grid1), dim3(kWave), 0, stream,
                        p);

@@ -63,8 +63,8 @@ struct CteParams {
   // 1e-6) rounded to bf16, to qn, kn, and writes beta = sigmoid(b_raw) and
   // g = -exp(A_log[h]) softplus(a_raw + dt_bias[h]) per token to g_out,
   // beta_out.  q, k, g, beta must point at qn, kn, g_out, beta_out, which
-  // the state pass reads.  qn, kn may alias q_raw, k_raw only when one wave
-  // serves all value heads of a key head (fused_inplace_ok).
+  // the state pass reads.  qn, kn may alias q_raw, k_raw only when one
+  // workgroup serves all value heads of a key head (fused_inplace_ok).
   const void* q_raw;
   const void* k_raw;
   const float* b_raw;
