@@ -5,12 +5,15 @@
 // [K, V] fp32 state plus a rank-1 update, so it is bound by HBM bandwidth:
 // the state is read once and written once and everything else is O(K + V).
 //
-//   thread t: float4 column group cg = t % 32 (columns 4cg..4cg+3) and row
-//   group rg = t / 32 (rows rg, rg+8, ..., rg+120): 16 float4 of state in
-//   registers, loaded before the prologue so the loads are in flight while
-//   wave 0 normalises q and k.
+//   thread t of NT: float4 column group cg = t % 32 (columns 4cg..4cg+3)
+//   and row group rg = t / 32 (rows rg, rg + NT/32, ...): 128 / (NT/32)
+//   float4 of state in registers, loaded before the prologue so the loads are
+//   in flight while wave 0 normalises q and k.  NT = 512 keeps 32 state
+//   floats per thread and the kernel under 64 VGPRs: eight waves per SIMD,
+//   so up to 1024 heads fill the chip in one round.  Larger launches run
+//   NT = 256 (16 float4 per thread).
 //
-//   r = S^T k^ and p = S^T q^ are reduced over the 8 row groups through LDS in
+//   r = S^T k^ and p = S^T q^ are reduced over the row groups through LDS in
 //   a fixed order (bitwise reproducible; one thread per column, so few
 //   registers are live next to the state), then per column
 //     u = beta (v - alpha r),  S' = alpha S + k^ u^T,  o = alpha p + (k^.q^) u
@@ -21,11 +24,10 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kColGroups = 32;                       // float4 column groups, V <= 128
-constexpr int kRowGroups = kThreads / kColGroups;    // 8
-constexpr int kRowsPerThread = 128 / kRowGroups;     // 16
+constexpr int kColGroups = 32;  // float4 column groups, V <= 128
 constexpr float kL2Eps = 1e-6f;
+// heads per round of the 512-thread form (four workgroups per CU)
+constexpr long kOneRound = 4 * 256;
 // buffer descriptor word 3 for raw (untyped, stride 0) buffers on gfx9-family parts
 constexpr int kBufferFlags = 0x00020000;
 // cache policy: non-temporal (the state is streamed exactly once each way)
@@ -44,8 +46,11 @@ __device__ __forceinline__ float4 load4<__bf16>(const __bf16* p) {
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
+template <typename T, int NT>
+__global__ __launch_bounds__(NT, 4) void tkg_kernel(const TkgParams p) {
+  constexpr int kThreads = NT;
+  constexpr int kRowGroups = kThreads / kColGroups;  // 16 or 8
+  constexpr int kRowsPerThread = 128 / kRowGroups;   // 8 or 16
   __shared__ float s_q[128];
   __shared__ float s_k[128];
   __shared__ float4 s_red[2][kRowGroups][kColGroups];  // partial S^T k^, S^T q^
@@ -62,11 +67,11 @@ __global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
   const bool col_ok = 4 * cg < V;
 
   // The head's state through buffer descriptors: one 32-bit VGPR offset per
-  // thread plus a uniform SGPR offset per row group keeps the 16 row
-  // addresses out of the VGPR budget.  K % 8 == 0, so row rg + 8i exists for
-  // every thread exactly when i < K/8 (uniform); threads past the last column
-  // group use an offset beyond the descriptor's range (loads return zero,
-  // stores are dropped).
+  // thread plus a uniform SGPR offset per row step keeps the row addresses
+  // out of the VGPR budget.  Steps i with kRowGroups * i >= K hold no row
+  // and are skipped (uniform); inside the last step, rows past K and threads
+  // past the last column group land beyond the descriptor's range (loads
+  // return zero, stores are dropped).
   const uint32_t head_bytes = (uint32_t)(K * V * 4);
   const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(p.state_in + (size_t)bh * K * V), (short)0, head_bytes, kBufferFlags);
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
       p.state_out + (size_t)bh * K * V, (short)0, head_bytes, kBufferFlags);
   const uint32_t voff = col_ok ? (uint32_t)((rg * V + 4 * cg) * 4) : 0x40000000u;
   const uint32_t row_step = (uint32_t)(kRowGroups * V * 4);
-  const int nrow = K / kRowGroups;
+  const int nrow = (K + kRowGroups - 1) / kRowGroups;
 
   // 1. this thread's state slab -> registers
   f4 s[kRowsPerThread];
@@ -122,8 +127,8 @@ __global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
   s_red[0][rg][cg] = pr;
   s_red[1][rg][cg] = pp;
   __syncthreads();
-  {
-    // thread t sums one of the 2 x 128 columns over the 8 row groups (fixed order)
+  if (tid < 256) {
+    // thread t sums one of the 2 x 128 columns over the row groups (fixed order)
     const float* red = reinterpret_cast<const float*>(s_red);
     const int which = tid / 128, col = tid % 128;
     float acc = red[(which * kRowGroups + 0) * 128 + col];
@@ -180,10 +185,19 @@ __global__ __launch_bounds__(kThreads, 4) void tkg_kernel(const TkgParams p) {
 
 hipError_t launch_tkg(const TkgParams& p, int dtype, hipStream_t stream) {
   if (p.BH == 0) return hipSuccess;
-  if (dtype == 1)
-    hipLaunchKernelGGL(tkg_kernel<__bf16>, dim3(p.BH), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(tkg_kernel<float>, dim3(p.BH), dim3(kThreads), 0, stream, p);
+  // 512 threads (eight waves per SIMD) when every head fits one round;
+  // beyond that 256 threads, whose larger slabs measured a little faster
+  const bool wide = p.BH <= kOneRound;
+  if (dtype == 1) {
+    if (wide)
+      hipLaunchKernelGGL((tkg_kernel<__bf16, 512>), dim3(p.BH), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((tkg_kernel<__bf16, 256>), dim3(p.BH), dim3(256), 0, stream, p);
+  } else if (wide) {
+    hipLaunchKernelGGL((tkg_kernel<float, 512>), dim3(p.BH), dim3(512), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((tkg_kernel<float, 256>), dim3(p.BH), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
