@@ -73,7 +73,10 @@ __device__ __forceinline__ void store2<__bf16>(__bf16* p, float a, float b) {
   *reinterpret_cast<uint32_t*>(p) = lo | (hi << 16);
 }
 
-// T (bf16 or fp32) workspace of one (batch*value head, chunk): T then P, each [C][C]
+// T (bf16 or fp32) workspace of one (batch*value head, chunk): fp32, T then
+// P, each [C][C]; bf16, the lower 16x16 blocks of T, then those of P, packed
+// as 16-byte items (block in row-major lower order, row, half) in the order
+// the state pass reads them
 template <typename T>
 __device__ __forceinline__ T* ws_chunk(void* ws, int bh, int NC, int c) {
   return static_cast<T*>(ws) + ((size_t)bh * NC + c) * 2 * kC * kC;
@@ -375,6 +378,7 @@ constexpr int kLB = 20;         // fp32 row pitch of a packed 16x16 block
 constexpr int kBlkF = 16 * kLB;  // floats per packed block
 constexpr int kPB = 24;         // bf16 row pitch of a packed P block
 constexpr int kNTri = kNB * (kNB + 1) / 2;
+constexpr int kTriItems = kNTri * 16 * 2;  // 16-byte bf16 items in the lower 16x16 blocks of a C x C tile
 
 __device__ __forceinline__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
 
@@ -679,31 +683,22 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
   }
   wave_lds_sync();
 
-  // lower blocks of T -> workspace in bf16, 16-byte stores (item: block,
-  // row, half); then P through the same buffer
+  // lower blocks of T -> workspace in bf16, packed (item it = 32 block + 2
+  // row + half holds 8 elements: the state pass reads them in this order, 1 KB
+  // per instruction), 16-byte stores; then P, packed the same way after T,
+  // through the same buffer
   T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
-  T* Pg = Tg + C * C;
-  auto item = [&](int q, int& blk, size_t& go, int& row, int& half) {
-    const int it = lane + kWave * q;
-    blk = it / 32;
-    row = (it % 32) / 2;
-    half = it % 2;
-    const int bi = blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0;
-    const int bj = blk - tri(bi, 0);
-    go = (size_t)(16 * bi + row) * C + 16 * bj + 8 * half;
-  };
+  T* Pg = Tg + kTriItems * 8;
 #pragma unroll
   for (int q = 0; q < kNTri * 32 / kWave; ++q) {
-    int blk, row, half;
-    size_t go;
-    item(q, blk, go, row, half);
+    const int it = lane + kWave * q, blk = it / 32, row = (it % 32) / 2, half = it % 2;
     const float* src = sA + blk * kBlkF + row * kLB + 8 * half;
     const float4 x0 = *reinterpret_cast<const float4*>(src);
     const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
     bf16x8 f;
     f[0] = f2bf(x0.x); f[1] = f2bf(x0.y); f[2] = f2bf(x0.z); f[3] = f2bf(x0.w);
     f[4] = f2bf(x1.x); f[5] = f2bf(x1.y); f[6] = f2bf(x1.z); f[7] = f2bf(x1.w);
-    *reinterpret_cast<uint4*>(Tg + go) = __builtin_bit_cast(uint4, f);
+    *reinterpret_cast<uint4*>(Tg + (size_t)it * 8) = __builtin_bit_cast(uint4, f);
   }
   T* sP = reinterpret_cast<T*>(sA);
   wave_lds_sync();
@@ -716,10 +711,9 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
   wave_lds_sync();
 #pragma unroll
   for (int q = 0; q < kNTri * 32 / kWave; ++q) {
-    int blk, row, half;
-    size_t go;
-    item(q, blk, go, row, half);
-    *reinterpret_cast<uint4*>(Pg + go) = *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
+    const int it = lane + kWave * q, blk = it / 32, row = (it % 32) / 2, half = it % 2;
+    *reinterpret_cast<uint4*>(Pg + (size_t)it * 8) =
+        *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
   }
 }
 
@@ -1070,7 +1064,6 @@ __device__ __forceinline__ Vec8<__bf16> k_tr_frag(const __bf16* m, int r0, int c
   return v;
 }
 
-constexpr int kTriItems = (kNB * (kNB + 1) / 2) * 16 * 2;  // 16-byte items in the lower blocks of a C x C tile
 
 template <int DK, int DVT, int MW>
 __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(const CteParams p) {
@@ -1105,6 +1098,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   constexpr bool KSW = DK == 128;
   constexpr int LDKS = KSW ? DK : LDK;
   __shared__ __align__(16) T sK[2][C * LDKS];
+  __shared__ __align__(16) T sQ[C * LDKS];  // Q of the chunk whose outputs the movers form
   __shared__ __align__(16) T sT[C * LDC];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
@@ -1176,7 +1170,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     const int rb = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
     const int cb = bi - rb * (rb + 1) / 2;
     const int row = 16 * rb + (it % 32) / 2, col = 16 * cb + 8 * (it % 2);
-    vo_tp[i] = it < kTriItems ? (uint32_t)(row * C + col) * ES : kOOB;
+    vo_tp[i] = it < kTriItems ? (uint32_t)it * 16u : kOOB;  // packed lower blocks
     lo_tp[i] = it < kTriItems ? row * LDC + col : 0;
   }
 #pragma unroll
@@ -1186,25 +1180,25 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     lo_v[i] = it < NVT ? t * LDV + c8 : 0;
   }
   // The outputs are computed by the movers, off the state chain: mover wave
-  // mw owns rows 16 mw .. +15 and holds their Q and P fragments (the MFMA
-  // first operand) in registers, loaded straight from HBM.
+  // mw owns rows 16 mw .. +15.  Q is staged in LDS like K (whole 1 KB runs
+  // per load instruction; its row fragments are read back from LDS); the P
+  // fragments (the MFMA first operand) sit in registers, loaded from the
+  // workspace.
   const int mw = w - kWaves;
   const int mnks = (16 * (mw + 1) + 31) / 32;  // k-steps of P touching lower blocks
-  uint32_t vo_qf[NQ], vo_pf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < NQ; ++s) {
-    const int k8 = 32 * s + 8 * lg;
-    vo_qf[s] = k8 < Dk ? (uint32_t)((16 * mw + lr) * Dk + k8) * ES : kOOB;
-  }
+  uint32_t vo_pf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    const int k8 = 32 * s + 8 * lg;  // upper blocks read as zero
-    vo_pf[s] = (s < mnks && (k8 >> 4) <= mw) ? (uint32_t)((16 * mw + lr) * C + k8) * ES : kOOB;
+    // packed lower blocks: row 16 mw + lr, columns k8 .. + 7 are item
+    // 32 tri(mw, k8 / 16) + 2 lr + (k8 / 8) % 2; upper blocks read as zero
+    const int k8 = 32 * s + 8 * lg, bj = k8 >> 4;
+    vo_pf[s] = (s < mnks && bj <= mw) ? (uint32_t)(32 * (mw * (mw + 1) / 2 + bj) + 2 * lr + ((k8 >> 3) & 1)) * 16u
+                                       : kOOB;
   }
-  // two register sets: the set of chunk c holds Q(c), P(c) and the K, V, g,
+  // two register sets: the set of chunk c holds P(c) and the Q, K, V, g,
   // beta, T of chunk c+1, so each load is issued two chunks before its use
   struct Regs {
-    V8 K[NKQ], Qf[NQ], Pf[KSTEPS], T[NTP], V[NVI];
+    V8 K[NKQ], Q[NKQ], Pf[KSTEPS], T[NTP], V[NVI];
     float g, b;
   };
   Regs rs0, rs1;
@@ -1221,17 +1215,17 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     for (int i = 0; i < NKQ; ++i) m.K[i] = V8::bload(r, vo_kq[i]);
   };
   auto ld_p = [&](Regs& m, int c) {
-    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + C * C, c < c_end ? (uint32_t)(C * C) * ES : 0u);
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c) + kTriItems * 8, c < c_end ? (uint32_t)kTriItems * 16u : 0u);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) m.Pf[s] = V8::bload(r, vo_pf[s]);
   };
   auto ld_q = [&](Regs& m, int c) {
     const auto r = make_rsrc(qg + (size_t)c * C * Dk, rem_bytes(c, Dk));
 #pragma unroll
-    for (int s = 0; s < NQ; ++s) m.Qf[s] = V8::bload(r, vo_qf[s]);
+    for (int i = 0; i < NKQ; ++i) m.Q[i] = V8::bload(r, vo_kq[i]);
   };
   auto ld_t = [&](Regs& m, int c) {
-    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < c_end ? (uint32_t)(C * C) * ES : 0u);
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < c_end ? (uint32_t)kTriItems * 16u : 0u);
 #pragma unroll
     for (int i = 0; i < NTP; ++i) m.T[i] = V8::bload(r, vo_tp[i]);
   };
@@ -1243,9 +1237,9 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     m.g = buf_load_f32(make_rsrc(gg + c * C, nb), (uint32_t)lane * 4u);
     m.b = buf_load_f32(make_rsrc(bg + c * C, nb), (uint32_t)lane * 4u);
   };
-  auto ld_all = [&](Regs& m, int c) {  // Q(c), P(c) and the rest of chunk c+1
+  auto ld_all = [&](Regs& m, int c) {  // P(c) and the rest of chunk c+1
     ld_p(m, c);
-    ld_q(m, c);
+    ld_q(m, c + 1);
     ld_k(m, c + 1);
     ld_vg(m, c + 1);
     ld_t(m, c + 1);
@@ -1253,6 +1247,10 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   auto st_k = [&](const Regs& m, int slot) {
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) m.K[i].store(sK[slot] + lo_kq[i]);
+  };
+  auto st_q = [&](const Regs& m) {
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) m.Q[i].store(sQ + lo_kq[i]);
   };
   auto st_tp = [&](T* dst, const V8* src) {
 #pragma unroll
@@ -1279,8 +1277,11 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
     for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
   };
-  auto out_qh = [&](f4* oacc, float4 eg, const V8* qf) {
+  auto out_qh = [&](f4* oacc, float4 eg) {
     const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
+    V8 qf[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) qf[s] = V8::load(sQ + kidx<KSW, LDKS>(16 * mw + lr, 32 * s + 8 * lg));
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
       f4 qh = {0.f, 0.f, 0.f, 0.f};
@@ -1309,11 +1310,12 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     ld_k(m, c + 3);
     flush_out(c - 1);
     f4 oacc[NVB];
-    out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]), m.Qf);
-    ld_q(m, c + 2);
+    out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]));
     __syncthreads();  // end of B
     st_vg(m);
     ld_vg(m, c + 3);
+    st_q(m);  // Q(c+1): every mover's Q(c) reads passed the barrier above
+    ld_q(m, c + 3);
     __syncthreads();  // end of C
     st_tp(sT, m.T);
     ld_t(m, c + 3);
@@ -1328,9 +1330,11 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     // instruction stream.
     __syncthreads();  // T zeroed, initial state staged
     ld_k(rs0, c_begin);
+    ld_q(rs0, c_begin);
     ld_vg(rs0, c_begin);
     ld_t(rs0, c_begin);
     st_k(rs0, c_begin & 1);
+    st_q(rs0);
     st_vg(rs0);
     st_tp(sT, rs0.T);
     ld_all(rs0, c_begin);
