@@ -376,7 +376,6 @@ __global__ __launch_bounds__(kThreads) void cte_local_kernel(const CteParams p) 
 //    the partial sums and the T blocks never leave the registers.
 constexpr int kLB = 20;         // fp32 row pitch of a packed 16x16 block
 constexpr int kBlkF = 16 * kLB;  // floats per packed block
-constexpr int kPB = 24;         // bf16 row pitch of a packed P block
 constexpr int kNTri = kNB * (kNB + 1) / 2;
 constexpr int kTriItems = kNTri * 16 * 2;  // 16-byte bf16 items in the lower 16x16 blocks of a C x C tile
 
@@ -398,8 +397,9 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
 // each then applies its own head's beta and decays.  Each wave owns one LDS
 // buffer of packed fp32 blocks that holds A, then T (the diagonal blocks of
 // T replace A's once the substitution has read them, the rest once the
-// levels are done), then P in bf16 for the stores, so two workgroups of two
-// waves fit per SIMD pair and one wave's loads overlap another's inverse.
+// levels are done), so two workgroups of two waves fit per SIMD pair and one
+// wave's loads overlap another's inverse.  P goes from the accumulators
+// straight to the workspace.
 // (The Neumann series needs the power and the running product side by side:
 // it keeps a second buffer.)
 // FUSE: the decode step's prologue is folded in (raw q, k and gates in; unit
@@ -685,8 +685,7 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
 
   // lower blocks of T -> workspace in bf16, packed (item it = 32 block + 2
   // row + half holds 8 elements: the state pass reads them in this order, 1 KB
-  // per instruction), 16-byte stores; then P, packed the same way after T,
-  // through the same buffer
+  // per instruction), 16-byte stores; then P, packed the same way after T
   T* Tg = ws_chunk<T>(p.ws, bh, NC, c);
   T* Pg = Tg + kTriItems * 8;
 #pragma unroll
@@ -700,20 +699,14 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
     f[4] = f2bf(x1.x); f[5] = f2bf(x1.y); f[6] = f2bf(x1.z); f[7] = f2bf(x1.w);
     *reinterpret_cast<uint4*>(Tg + (size_t)it * 8) = __builtin_bit_cast(uint4, f);
   }
-  T* sP = reinterpret_cast<T*>(sA);
-  wave_lds_sync();
+  // P straight from the accumulators: lane (lr, lg) of block b holds row
+  // lr, columns 4 lg .. + 3, i.e. half lg / 2 of item 32 b + 2 lr + lg / 2,
+  // so a block is one contiguous 512-byte store
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
-#pragma unroll
-    for (int j = 0; j <= i; ++j)
-      store4<T>(sP + tri(i, j) * 16 * kPB + lr * kPB + 4 * lg, pacc[tri(i, j)][0], pacc[tri(i, j)][1],
-                pacc[tri(i, j)][2], pacc[tri(i, j)][3]);
-  wave_lds_sync();
-#pragma unroll
-  for (int q = 0; q < kNTri * 32 / kWave; ++q) {
-    const int it = lane + kWave * q, blk = it / 32, row = (it % 32) / 2, half = it % 2;
-    *reinterpret_cast<uint4*>(Pg + (size_t)it * 8) =
-        *reinterpret_cast<const uint4*>(sP + blk * 16 * kPB + row * kPB + 8 * half);
+  for (int b = 0; b < kNTri; ++b) {
+    bf16x4 y;
+    y[0] = f2bf(pacc[b][0]); y[1] = f2bf(pacc[b][1]); y[2] = f2bf(pacc[b][2]); y[3] = f2bf(pacc[b][3]);
+    *reinterpret_cast<bf16x4*>(Pg + (size_t)(32 * b + 2 * lr) * 8 + 4 * lg) = y;
   }
 }
 
