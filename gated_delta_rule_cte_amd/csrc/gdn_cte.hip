@@ -391,10 +391,13 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
   return c;
 }
 
-// One workgroup per (chunk, key head, NG value heads of its GQA group), one
-// wave per value head.  The waves of a workgroup load the same K and Q rows
-// (the second read hits the cache) and form the same raw K K^T and Q K^T;
-// each then applies its own head's beta and decays.  Each wave owns one LDS
+// One workgroup per (chunk, key head, NG * NH value heads of its GQA group):
+// NG waves of NH value heads each, taken in turn.  The waves of a workgroup
+// load the same K and Q rows (the second read hits the cache) and form the
+// same raw K K^T and Q K^T; each head then gets its own beta and decays.
+// The plain prefill runs one head per wave (NG = 2, NH = 1); the folded
+// prologue runs one wave for both heads of a pair (NG = 1, NH = 2), since
+// its unit rows replace the raw ones in place.  Each wave owns one LDS
 // buffer of packed fp32 blocks that holds A, then T (the diagonal blocks of
 // T replace A's once the substitution has read them, the rest once the
 // levels are done), so two workgroups of two waves fit per SIMD pair and one
@@ -404,7 +407,7 @@ __device__ __forceinline__ f4 mfma4_f32(float4 a4, f4 b, f4 c) {
 // it keeps a second buffer.)
 // FUSE: the decode step's prologue is folded in (raw q, k and gates in; unit
 // rows of q, k and beta, g out for the state pass), see CteParams.
-template <int DK, int NG, int ALGO, bool FUSE>
+template <int DK, int NG, int NH, int ALGO, bool FUSE>
 __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams p) {
   using T = __bf16;
   using V8 = Vec8<T>;
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
   __shared__ __align__(16) float sGamW[NG][C];
   __shared__ __align__(16) float sBetaW[NG][C];
 
-  const int w = threadIdx.x >> 6;  // value head hh0 + w of the group
+  const int w = threadIdx.x >> 6;  // value heads hh0 + NH w .. + NH - 1 of the group
   const int lane = threadIdx.x & (kWave - 1), lr = lane & 15, lg = lane >> 4;
   float* const sA = sbuf[w][0];
   float* const sGam = sGamW[w];
@@ -425,13 +428,13 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
   const int NC = (S + C - 1) / C;
   const int G = Hv / Hk;
   const int lid = xcd_logical_id(blockIdx.x, (int)gridDim.x);
-  const int GN = G / NG;  // value-head groups per key head
-  const int hh0 = (lid % GN) * NG;
+  const int GN = G / (NG * NH);  // value-head groups per key head
+  const int hh0 = (lid % GN) * NG * NH;
   const int nseg = p.c_end - p.c_begin;
   const int c = p.c_begin + (lid / GN) % nseg;
   const int bhk = lid / (GN * nseg);
   const int b = bhk / Hk, hk = bhk - b * Hk;
-  const int bh = b * Hv + hk * G + hh0 + w;  // this wave's value head
+  const int bh0 = b * Hv + hk * G + hh0 + NH * w;  // this wave's first value head
   const int c0 = c * C;
   const uint32_t rem = (uint32_t)(S - c0);
 
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
       kf[rb][s] = V8::bload(rK, off);
       qf[rb][s] = V8::bload(rQ, off);
     }
-  float gln, ben;
+  float gln[NH], ben[NH];
   if constexpr (FUSE) {
     // Each row made unit length: lane (lr, lg) holds 8 columns of row
     // 16 rb + lr in each of its NS fragments, the rest of the row is in lanes
@@ -501,19 +504,25 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
     // beta = sigmoid(b), g = -exp(A_log[h]) softplus(a + dt_bias[h]) for the
     // token of this lane; zero past the sequence end
     const bool tv = c0 + lane < S;
-    const size_t row = (size_t)bh * S + c0;
-    const int h = bh % Hv;
-    const float bb = buf_load_f32(make_rsrc(p.b_raw + row, rem * 4u), (uint32_t)lane * 4u);
-    const float aa = buf_load_f32(make_rsrc(p.a_raw + row, rem * 4u), (uint32_t)lane * 4u);
-    gln = tv ? -expf(p.A_log[h]) * softplusf_(aa + p.dt_bias[h]) : 0.f;
-    ben = tv ? sigmoidf_(bb) : 0.f;
-    if (tv) {
-      p.g_out[row + lane] = gln;
-      p.beta_out[row + lane] = ben;
+#pragma unroll
+    for (int n = 0; n < NH; ++n) {
+      const size_t row = (size_t)(bh0 + n) * S + c0;
+      const int h = (bh0 + n) % Hv;
+      const float bb = buf_load_f32(make_rsrc(p.b_raw + row, rem * 4u), (uint32_t)lane * 4u);
+      const float aa = buf_load_f32(make_rsrc(p.a_raw + row, rem * 4u), (uint32_t)lane * 4u);
+      gln[n] = tv ? -expf(p.A_log[h]) * softplusf_(aa + p.dt_bias[h]) : 0.f;
+      ben[n] = tv ? sigmoidf_(bb) : 0.f;
+      if (tv) {
+        p.g_out[row + lane] = gln[n];
+        p.beta_out[row + lane] = ben[n];
+      }
     }
   } else {
-    gln = buf_load_f32(make_rsrc(p.g + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
-    ben = buf_load_f32(make_rsrc(p.beta + (size_t)bh * S + c0, rem * 4u), (uint32_t)lane * 4u);
+#pragma unroll
+    for (int n = 0; n < NH; ++n) {
+      gln[n] = buf_load_f32(make_rsrc(p.g + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+      ben[n] = buf_load_f32(make_rsrc(p.beta + (size_t)(bh0 + n) * S + c0, rem * 4u), (uint32_t)lane * 4u);
+    }
   }
 
   // raw products of the lower blocks, transposed: lane holds row 16 i + lr,
@@ -534,8 +543,12 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
     }
   const float scale = p.scale;
 
-  sGam[lane] = wave_inclusive_scan_dpp(gln);
-  sBeta[lane] = ben;
+#pragma unroll
+  for (int n = 0; n < NH; ++n) {
+  const int bh = bh0 + n;
+  if (n > 0) wave_lds_sync();  // the previous head's reads of the buffer are done
+  sGam[lane] = wave_inclusive_scan_dpp(gln[n]);
+  sBeta[lane] = ben[n];
   wave_lds_sync();
 
   // A (packed, fp32) and P (registers).  Below the diagonal block every
@@ -708,6 +721,7 @@ __global__ __launch_bounds__(kWave * NG) void cte_local1_kernel(const CteParams 
     y[0] = f2bf(pacc[b][0]); y[1] = f2bf(pacc[b][1]); y[2] = f2bf(pacc[b][2]); y[3] = f2bf(pacc[b][3]);
     *reinterpret_cast<bf16x4*>(Pg + (size_t)(32 * b + 2 * lr) * 8 + 4 * lg) = y;
   }
+  }  // value heads of this wave
 }
 
 // ===========================================================================
@@ -1431,24 +1445,28 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 }
 
 // one workgroup per (chunk, key head, pair of value heads) when the GQA group
-// is even, else per (chunk, value head); one wave per value head
+// is even, else per (chunk, value head); one wave per value head, or with the
+// folded prologue one wave for the pair
 constexpr int local1_ng(int Hk, int Hv) { return (Hv / Hk) % 2 == 0 ? 2 : 1; }
+
+template <int DK, int NG, int NH, bool FUSE>
+void launch_local1_as(const CteParams& p, long wgs, bool neu, hipStream_t stream) {
+  if (neu)
+    hipLaunchKernelGGL((cte_local1_kernel<DK, NG, NH, kAlgoNeumann, FUSE>), dim3((unsigned)wgs), dim3(NG * kWave), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((cte_local1_kernel<DK, NG, NH, 0, FUSE>), dim3((unsigned)wgs), dim3(NG * kWave), 0, stream, p);
+}
 
 template <int DK, bool FUSE>
 hipError_t launch_local1(const CteParams& p, long grid1, hipStream_t stream) {
   const bool neu = p.algo == kAlgoNeumann;
-  if (local1_ng(p.Hk, p.Hv) == 2) {
-    if (neu)
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, kAlgoNeumann, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(2 * kWave),
-                         0, stream, p);
-    else
-      hipLaunchKernelGGL((cte_local1_kernel<DK, 2, 0, FUSE>), dim3((unsigned)(grid1 / 2)), dim3(2 * kWave), 0, stream,
-                         p);
-  } else if (neu)
-    hipLaunchKernelGGL((cte_local1_kernel<DK, 1, kAlgoNeumann, FUSE>), dim3((unsigned)grid1), dim3(kWave), 0, stream,
-                       p);
+  if (local1_ng(p.Hk, p.Hv) == 1)
+    launch_local1_as<DK, 1, 1, FUSE>(p, grid1, neu, stream);
+  else if constexpr (FUSE)
+    launch_local1_as<DK, 1, 2, FUSE>(p, grid1 / 2, neu, stream);  // one wave rewrites each key head's rows
   else
-    hipLaunchKernelGGL((cte_local1_kernel<DK, 1, 0, FUSE>), dim3((unsigned)grid1), dim3(kWave), 0, stream, p);
+    launch_local1_as<DK, 2, 1, FUSE>(p, grid1 / 2, neu, stream);
   return hipGetLastError();
 }
 
