@@ -1106,6 +1106,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   constexpr int LDKS = KSW ? DK : LDK;
   __shared__ __align__(16) T sK[2][C * LDKS];
   __shared__ __align__(16) T sQ[C * LDKS];  // Q of the chunk whose outputs the movers form
+  __shared__ __align__(16) float sQH[kWaves * NVB * kWave * 4];  // scale Gam Q H, row block w, from wave w
   __shared__ __align__(16) T sT[C * LDC];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
@@ -1186,11 +1187,11 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     vo_v[i] = (it < NVT && col0 + c8 < Dv) ? (uint32_t)(t * Dv + col0 + c8) * ES : kOOB;
     lo_v[i] = it < NVT ? t * LDV + c8 : 0;
   }
-  // The outputs are computed by the movers, off the state chain: mover wave
+  // The outputs are finished by the movers, off the state chain: mover wave
   // mw owns rows 16 mw .. +15.  Q is staged in LDS like K (whole 1 KB runs
-  // per load instruction; its row fragments are read back from LDS); the P
-  // fragments (the MFMA first operand) sit in registers, loaded from the
-  // workspace.
+  // per load instruction; compute wave mw reads its row fragments for
+  // Q H); the P fragments (the MFMA first operand of P U) sit in the mover's
+  // registers, loaded from the workspace.
   const int mw = w - kWaves;
   const int mnks = (16 * (mw + 1) + 31) / 32;  // k-steps of P touching lower blocks
   uint32_t vo_pf[KSTEPS];
@@ -1284,20 +1285,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
     for (int i = 0; i < NVI; ++i) V8::load(sO + lo_v[i]).bstore(ro, vo_v[i]);
   };
-  auto out_qh = [&](f4* oacc, float4 eg) {
-    const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
-    V8 qf[NQ];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) qf[s] = V8::load(sQ + kidx<KSW, LDKS>(16 * mw + lr, 32 * s + 8 * lg));
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      f4 qh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NQ; ++s) qh = MM::mma(qf[s], V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg), qh);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[vb][r] = scale * egv[r] * qh[r];
-    }
-  };
   auto out_pu = [&](f4* oacc, const V8* pf) {
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -1310,14 +1297,13 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     }
   };
   // one chunk of mover work; m is the set of chunk c, refilled for chunk c+2.
-  // scale Gam Q H while the compute waves run B (H of chunk c is in LDS
-  // then), + P U once U is there.
+  // The outputs: compute wave w leaves scale Gam Q H of row block w in LDS
+  // during B (H of chunk c is in LDS then); mover wave w adds P U once U is
+  // there.
   auto mover_chunk = [&](Regs& m, int c) {
     st_k(m, (c + 1) & 1);
     ld_k(m, c + 3);
     flush_out(c - 1);
-    f4 oacc[NVB];
-    out_qh(oacc, *reinterpret_cast<const float4*>(&sEG[16 * mw + 4 * lg]));
     __syncthreads();  // end of B
     st_vg(m);
     ld_vg(m, c + 3);
@@ -1326,6 +1312,9 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     __syncthreads();  // end of C
     st_tp(sT, m.T);
     ld_t(m, c + 3);
+    f4 oacc[NVB];
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) oacc[vb] = *reinterpret_cast<const f4*>(sQH + ((mw * NVB + vb) * kWave + lane) * 4);
     out_pu(oacc, m.Pf);
     ld_p(m, c + 2);
     __syncthreads();  // end of D
@@ -1375,14 +1364,25 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
       const float Gt[4] = {eg.x, eg.y, eg.z, eg.w}, bt[4] = {be.x, be.y, be.z, be.w};
       dt[0] = ed.x; dt[1] = ed.y; dt[2] = ed.z; dt[3] = ed.w;
       GC = sEG[C - 1];
-      V8 kf[NQ];
+      // and the outputs' first part, scale Gam Q H of row block w (the same
+      // state operands), left in LDS for mover wave w
+      V8 kf[NQ], qf[NQ];
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) kf[s] = V8::load(sKc + kidx<KSW, LDKS>(16 * w + lr, 32 * s + 8 * lg));
+      for (int s = 0; s < NQ; ++s) {
+        kf[s] = V8::load(sKc + kidx<KSW, LDKS>(16 * w + lr, 32 * s + 8 * lg));
+        qf[s] = V8::load(sQ + kidx<KSW, LDKS>(16 * w + lr, 32 * s + 8 * lg));
+      }
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        f4 kh = {0.f, 0.f, 0.f, 0.f};
+        f4 kh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NQ; ++s) kh = MM::mma(kf[s], V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg), kh);
+        for (int s = 0; s < NQ; ++s) {
+          const V8 hf = V8::load(sHt + (16 * vb + lr) * LDK + 32 * s + 8 * lg);
+          kh = MM::mma(kf[s], hf, kh);
+          qh = MM::mma(qf[s], hf, qh);
+        }
+        *reinterpret_cast<f4*>(sQH + ((w * NVB + vb) * kWave + lane) * 4) =
+            f4{scale * Gt[0] * qh[0], scale * Gt[1] * qh[1], scale * Gt[2] * qh[2], scale * Gt[3] * qh[3]};
         const uint2 v4 = lds_tr4(sV, LDV, 16 * w + 4 * lg, 16 * vb, lane);  // V[16 w + 4 lg + r][16 vb + lr]
         float x[4];
 #pragma unroll
