@@ -57,8 +57,8 @@ OP_SOURCES = {
 }
 # kernels of each entry point in the bench workloads: (name fragment, grid in threads or None)
 OP_KERNELS = {
-    "cte": [("cte_local1_kernel<128, 2, 0, false>", 1 * 32 * 64 // 2 * 128), ("cte_state_ws_kernel<128, 16,", None)],
-    "cte_long": [("cte_local1_kernel<128, 2, 0, false>", 4 * 32 * 256 // 2 * 128), ("cte_state_ws_kernel<128, 64,", None)],
+    "cte": [("cte_local1_kernel<128, 2, 1, 0, false>", 1 * 32 * 64 // 2 * 128), ("cte_state_ws_kernel<128, 16,", None)],
+    "cte_long": [("cte_local1_kernel<128, 2, 1, 0, false>", 4 * 32 * 256 // 2 * 128), ("cte_state_ws_kernel<128, 64,", None)],
     "tkg": [("tkg_kernelIDF16bLi512E", 1024 * 512)],          # the 512-thread form (mangled name)
     "block": [("block_proj", None), ("tkg_kernelIDF16bLi256E", 2048 * 256)],
 }
