@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_tkg.hip", "gdn_cte.hip", "gdn_block.hip", "gdn_fused.hip", "gdn_block_cte.hip",
-           "gdn_noalloc.hip"]
+           "gdn_noalloc.hip", "gdn_blas.cpp"]
 # measurement aids for bench.py, in a library of their own
 CALIB_LIB = os.path.join(PKG, "libgdn_calib.so")
 CALIB_SOURCES = ["gdn_calib.hip"]
@@ -90,7 +90,8 @@ def _link(sources, out, verbose, extra_flags, build_dir=BUILD_DIR):
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(one, sources))
     tmp = out + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    libs = ["-lhipblaslt"] if "gdn_blas.cpp" in sources else []
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *libs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

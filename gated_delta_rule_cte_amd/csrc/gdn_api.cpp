@@ -396,20 +396,28 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
     return launched(e);
   }
   char* w = static_cast<char*>(workspace);
-  // the four projections in one launch; a and b join it when their rows are
-  // whole 16-byte pieces, else they take one wave per token
+  // The four projections are plain GEMMs and go to the vendor library; what
+  // it does not take runs in one launch of gemm_bf16_kernel (a and b join the
+  // GEMMs when their rows are whole 16-byte pieces, else they take one wave
+  // per token).
   const bool ab_gemm = Hv % 8 == 0;
   gdn::GemmParams gp{};
   gp.A = hidden; gp.M = (int)M; gp.K = H;
-  gp.B[0] = W_in_qkv; gp.C[0] = w + L.mixed; gp.N[0] = (int)conv_dim;
-  gp.B[1] = W_in_z; gp.C[1] = w + L.ztok; gp.N[1] = (int)value_dim;
-  gp.nprob = 2;
+  auto add = [&](const void* Wm, void* Cm, int N) {
+    gp.B[gp.nprob] = Wm; gp.C[gp.nprob] = Cm; gp.N[gp.nprob] = N;
+    ++gp.nprob;
+  };
+  if (gdn::gemm_bf16_library(hidden, W_in_qkv, w + L.mixed, (int)M, (int)conv_dim, H, hs) != hipSuccess)
+    add(W_in_qkv, w + L.mixed, (int)conv_dim);
+  if (gdn::gemm_bf16_library(hidden, W_in_z, w + L.ztok, (int)M, (int)value_dim, H, hs) != hipSuccess)
+    add(W_in_z, w + L.ztok, (int)value_dim);
   if (ab_gemm) {
-    gp.B[2] = W_in_a; gp.C[2] = w + L.abtok; gp.N[2] = Hv;
-    gp.B[3] = W_in_b; gp.C[3] = w + L.abtok + M * Hv * 2; gp.N[3] = Hv;
-    gp.nprob = 4;
+    if (gdn::gemm_bf16_library(hidden, W_in_a, w + L.abtok, (int)M, Hv, H, hs) != hipSuccess)
+      add(W_in_a, w + L.abtok, Hv);
+    if (gdn::gemm_bf16_library(hidden, W_in_b, w + L.abtok + M * Hv * 2, (int)M, Hv, H, hs) != hipSuccess)
+      add(W_in_b, w + L.abtok + M * Hv * 2, Hv);
   }
-  if ((e = gdn::launch_gemm_bf16(gp, hs)) != hipSuccess) return launched(e);
+  if (gp.nprob > 0 && (e = gdn::launch_gemm_bf16(gp, hs)) != hipSuccess) return launched(e);
   if (!ab_gemm) {
     gdn::NarrowParams na{hidden, W_in_a, W_in_b, reinterpret_cast<float*>(w + L.a),
                          reinterpret_cast<float*>(w + L.b), (int)M, Hv, H, S};

@@ -123,6 +123,10 @@ struct GemmParams {
   int N[4];
 };
 hipError_t launch_gemm_bf16(const GemmParams& g, hipStream_t stream);
+// C[M, N] = A[M, K] B[K, N], row-major bf16 (leading dimensions K, N, N), fp32
+// accumulation, through the vendor GEMM library; hipErrorNotSupported when
+// the library cannot take the product (nothing was queued then)
+hipError_t gemm_bf16_library(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t stream);
 struct NarrowParams {
   const void* A;             // [M, K] bf16, M = B * S token rows
   const void* Wa;            // [K, N] bf16
