@@ -55,13 +55,18 @@ OP_SOURCES = {
     "tkg": ["gdn_api.cpp", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
     "block": ["gdn_api.cpp", "gdn_block.hip", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
 }
-# kernels of each entry point in the bench workloads: (name fragment, grid in threads or None)
+# kernels of each entry point in the bench workloads: (name fragment, grid in
+# threads or None, launches per call).  The decode layer's decode-step launches
+# (two of 1024 heads) have the same name and grid as gdn_tkg's: record_traffic
+# tells them apart by the projection launch they follow.
 OP_KERNELS = {
-    "cte": [("cte_local1_kernel<128, 2, 1, 0, false>", 1 * 32 * 64 // 2 * 128), ("cte_state_ws_kernel<128, 16,", None)],
-    "cte_long": [("cte_local1_kernel<128, 2, 1, 0, false>", 4 * 32 * 256 // 2 * 128), ("cte_state_ws_kernel<128, 64,", None)],
-    "tkg": [("tkg_kernelIDF16bLi512E", 1024 * 512)],          # the 512-thread form (mangled name)
-    "block": [("block_proj", None), ("tkg_kernelIDF16bLi256E", 2048 * 256)],
+    "cte": [("cte_local1_kernel<128, 2, 1, 0, false>", 1 * 32 * 64 // 2 * 128, 1), ("cte_state_ws_kernel<128, 16,", None, 1)],
+    "cte_long": [("cte_local1_kernel<128, 2, 1, 0, false>", 4 * 32 * 256 // 2 * 128, 1),
+                 ("cte_state_ws_kernel<128, 64,", None, 1)],
+    "tkg": [("tkg_kernelIDF16bLi512E", 1024 * 512, 1)],       # the 512-thread form (mangled name)
+    "block": [("block_proj", None, 1), ("tkg_kernelIDF16bLi512E", 1024 * 512, 2)],
 }
+BLOCK_TKG_LAUNCHES = 2
 COPY_CAL_BYTES = 512 << 20
 
 CTE = dict(B=1, Hk=16, Hv=32, S=4096, Dk=128, Dv=128)
@@ -146,11 +151,21 @@ def record_traffic(d):
     import csv
 
     def per_kernel(path):
-        acc = {}
+        # average per (kernel, grid, caller); caller "block" marks the
+        # decode-step launches that follow a decode-layer projection
         with open(path) as fh:
-            for row in csv.DictReader(fh):
-                key = (row["Kernel_Name"], int(row["Grid_Size"]))
-                acc.setdefault(key, []).append(float(row["Counter_Value"]))
+            rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Dispatch_Id"]))
+        acc, pending = {}, 0
+        for row in rows:
+            name = row["Kernel_Name"]
+            caller = ""
+            if "block_proj" in name:
+                pending = BLOCK_TKG_LAUNCHES
+            elif "tkg_kernel" in name and pending > 0:
+                caller, pending = "block", pending - 1
+            else:
+                pending = 0
+            acc.setdefault((name, int(row["Grid_Size"]), caller), []).append(float(row["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
     f = per_kernel(os.path.join(d, "bench_FETCH_SIZE_counter_collection.csv"))
@@ -163,14 +178,16 @@ def record_traffic(d):
     ops = {}
     for op, specs in OP_KERNELS.items():
         kern, total = {}, 0.0
-        for frag, grid in specs:
-            keys = [k for k in f if frag in k[0] and "rocclr" not in k[0] and (grid is None or k[1] == grid)]
+        caller = "block" if op == "block" else ""
+        for frag, grid, launches in specs:
+            keys = [k for k in f if frag in k[0] and "rocclr" not in k[0] and (grid is None or k[1] == grid)
+                    and k[2] == caller]
             if len(keys) != 1:
                 raise SystemExit(f"record-traffic: {op}: expected one kernel matching {frag!r}, found {keys}")
             k = keys[0]
-            by = (f[k] * ff + w[k] * wf) * 1024
-            kern[k[0]] = {"grid_threads": k[1], "FETCH_SIZE_KiB": f[k], "WRITE_SIZE_KiB": w[k],
-                          "bytes_calibrated": by}
+            by = (f[k] * ff + w[k] * wf) * 1024 * launches
+            kern[k[0]] = {"grid_threads": k[1], "launches_per_call": launches, "FETCH_SIZE_KiB": f[k],
+                          "WRITE_SIZE_KiB": w[k], "bytes_calibrated": by}
             total += by
         ops[op] = {"bytes_per_call": total, "kernels": kern}
     rec = {"calibration": {"copy_bytes": COPY_CAL_BYTES, "copy_kernel": ck[0], "FETCH_SIZE_KiB": cf[ck],
@@ -180,6 +197,22 @@ def record_traffic(d):
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps({op: v["bytes_per_call"] for op, v in ops.items()}))
+
+
+def warm_replays(graph, stream, torch, min_ms=60.0):
+    """Replay `graph` on `stream` until at least `min_ms` of GPU time has passed.
+    Right after a capture (the GPU idle meanwhile) the first tens of
+    milliseconds of calls run up to 25 % slower than the steady state, so every
+    timed region here follows such a warm-up."""
+    done = 0.0
+    while done < min_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        e1.synchronize()
+        done += e0.elapsed_time(e1)
 
 
 def prefill_layer(gdn, torch, dev, inputs):
@@ -218,9 +251,9 @@ def prefill_layer(gdn, torch, dev, inputs):
                 call(sets[r])
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
+    reps = 20
+    warm_replays(graph, stream, torch)
     with torch.cuda.stream(stream):
-        graph.replay()
         ev0.record(stream)
         for _ in range(reps):
             graph.replay()
@@ -271,8 +304,8 @@ def fused_prefill(gdn, torch, dev, inputs):
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 12
+    warm_replays(graph, stream, torch)
     with torch.cuda.stream(stream):
-        graph.replay()
         ev0.record(stream)
         for _ in range(reps):
             graph.replay()
@@ -320,8 +353,8 @@ def compare_inverse(gdn, torch, dev):
             torch.cuda.synchronize()
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = max(2, int(2e5 // S))
+            warm_replays(graph, stream, torch, min_ms=30.0)
             with torch.cuda.stream(stream):
-                graph.replay()
                 ev0.record(stream)
                 for _ in range(reps):
                     graph.replay()
@@ -360,14 +393,14 @@ def long_inputs(gdn, torch, dev):
     return single
 
 
-def long_prefill(gdn, torch, dev, reps=5):
+def long_prefill(gdn, torch, dev, reps=10):
     """gdn_cte at B=4, Hk=16, Hv=32, S=16384, D=128, bf16, zero initial state:
     the single call, and the same sequence as four chained S=4096 calls, each
     carrying the state to the next.  Inputs drawn on the device with the
     workload's distributions (q, k unit rows; g ~ U(-0.3, -0.005); beta ~
     U(0.05, 0.95)); one call moves 1.6 GB, far above the 256 MB Infinity
     Cache, so one input set suffices.  Graphs of 2 single calls / 2 chains,
-    HIP events on the replay stream."""
+    HIP events on the replay stream, after warm_replays."""
     B, Hk, Hv, S, D = 4, 16, 32, 16384, 128
     gen = torch.Generator(device=dev)
     gen.manual_seed(4)
@@ -404,8 +437,8 @@ def long_prefill(gdn, torch, dev, reps=5):
                 fn()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm_replays(graph, stream, torch)
         with torch.cuda.stream(stream):
-            graph.replay()
             ev0.record(stream)
             for _ in range(reps):
                 graph.replay()
@@ -530,7 +563,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--op-iters", type=int, default=200, help="calls per entry point for per-op times")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--no-long", action="store_true",
@@ -724,7 +757,7 @@ def main():
 
     per_op_ms = {}
     for name, _, _ in ops:
-        timed(op_graphs[name], 1)
+        warm_replays(op_graphs[name][0], stream, torch, min_ms=30.0)
         reps = max(1, args.op_iters // OP_REP)
         per_op_ms[name] = timed(op_graphs[name], reps) / OP_REP
 

@@ -32,6 +32,7 @@ struct TkgParams {
   void* out;  // bf16 [BH, V]
   int BH, Hv, K, V;
   float rms_eps;
+  int bh0;  // first head of a launch (set by launch_tkg)
 };
 // dtype: 0 fp32, 1 bf16 (q, k, v, z)
 hipError_t launch_tkg(const TkgParams& p, int dtype, hipStream_t stream);
