@@ -178,8 +178,8 @@ def record_traffic(d):
     ops = {}
     for op, specs in OP_KERNELS.items():
         kern, total = {}, 0.0
-        caller = "block" if op == "block" else ""
         for frag, grid, launches in specs:
+            caller = "block" if op == "block" and "tkg_kernel" in frag else ""
             keys = [k for k in f if frag in k[0] and "rocclr" not in k[0] and (grid is None or k[1] == grid)
                     and k[2] == caller]
             if len(keys) != 1:
