@@ -303,7 +303,7 @@ int gdn_cte_fused(const void* q, const void* k, const void* v, const float* b, c
 // ------------------------------------------------------------ gdn_block_cte
 namespace {
 struct BlockCteLayout {
-  size_t mixed, ztok, abtok, q, k, v, zh, a, b, g, beta, o, cte, total;  // byte offsets and total size
+  size_t mixed, ztok, abtok, q, k, v, a, b, g, beta, o, cte, total;  // byte offsets and total size
 };
 BlockCteLayout block_cte_layout(int B, int S, int Hk, int Hv, int Dk, int Dv) {
   BlockCteLayout L{};
@@ -316,7 +316,6 @@ BlockCteLayout block_cte_layout(int B, int S, int Hk, int Hv, int Dk, int Dv) {
   L.q = off; off += align256(M * key_dim * 2);
   L.k = off; off += align256(M * key_dim * 2);
   L.v = off; off += align256(M * value_dim * 2);
-  L.zh = off; off += align256(M * value_dim * 2);
   L.a = off; off += nh;
   L.b = off; off += nh;
   L.g = off; off += nh;
@@ -428,7 +427,8 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   cs.a_head = reinterpret_cast<float*>(w + L.a);
   cs.b_head = reinterpret_cast<float*>(w + L.b);
   cs.mixed = w + L.mixed; cs.z_tok = w + L.ztok; cs.conv_weight = conv_weight; cs.conv_state = conv_state_in;
-  cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v; cs.z_head = w + L.zh;
+  // z stays token-major: the output norm reads it there
+  cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v; cs.z_head = nullptr;
   cs.B = B; cs.S = S; cs.conv_dim = (int)conv_dim; cs.value_dim = (int)value_dim; cs.key_dim = (int)key_dim;
   cs.Hk = Hk; cs.Hv = Hv; cs.Dk = Dk; cs.Dv = Dv; cs.K_win = K_win;
   if ((e = gdn::launch_conv_split(cs, hs)) != hipSuccess) return launched(e);
@@ -457,9 +457,9 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   p.ws = w + L.cte;
   if ((e = gdn::launch_cte(p, GDN_BF16, hs)) != hipSuccess) return launched(e);
   gdn::FusedPost post{};
-  post.out = w + L.o; post.z = w + L.zh; post.norm_weight = norm_weight;
+  post.out = w + L.o; post.z = w + L.ztok; post.norm_weight = norm_weight;
   post.rows = (long)B * Hv * S; post.Dv = Dv; post.rms_eps = rms_eps;
-  post.out_tok = out; post.S = S; post.Hv = Hv;
+  post.out_tok = out; post.S = S; post.Hv = Hv; post.z_token_major = 1;
   return launched(gdn::launch_fused_post(post, GDN_BF16, hs));
 }
 

@@ -11,7 +11,7 @@
 //                        reads, outputs staged through LDS for 16-byte stores;
 //   proj_narrow_kernel   the a and b projections (N = Hv), one wave per token;
 //   conv_split_kernel    conv + silu over the sequence, split into head-major
-//                        q, k, v (and z), rounded to bf16;
+//                        q, k, v (and z when asked), rounded to bf16;
 //   conv_window_kernel   the conv window after the last token.
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -191,7 +191,7 @@ __device__ __forceinline__ void unpack8(uint4 u, float* e) {
 
 template <int KW>
 __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitParams p) {
-  const int gconv = p.conv_dim / 8, gz = p.value_dim / 8, gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
+  const int gconv = p.conv_dim / 8, gz = p.z_head ? p.value_dim / 8 : 0, gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
   const int ngrp = gconv + gz + gab;
   const int ntb = (p.S + kConvTok - 1) / kConvTok;
   const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
@@ -344,7 +344,8 @@ hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream) {
 
 hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
   const int gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
-  const long n = (long)p.B * ((p.S + kConvTok - 1) / kConvTok) * ((p.conv_dim + p.value_dim) / 8 + gab);
+  const int gz = p.z_head ? p.value_dim / 8 : 0;
+  const long n = (long)p.B * ((p.S + kConvTok - 1) / kConvTok) * (p.conv_dim / 8 + gz + gab);
   if (n > 0) {
     const dim3 grid((unsigned)((n + kGThreads - 1) / kGThreads)), block(kGThreads);
     switch (p.K_win) {

@@ -9,7 +9,8 @@
 //   l2norm_rows_kernel    q^, k^ = x / sqrt(sum x^2 + 1e-6), rounded to the compute type;
 //   gates_kernel          beta and g per token of every value head (A_log, dt_bias by head);
 //   (gdn_cte with scale = Dk^-1/2 on q^, k^, v, g, beta)
-//   rms_gate_rows_kernel  y = w * o / sqrt(mean(o^2) + eps) * silu(z) over Dv, in place.
+//   rms_gate_rows_kernel  y = w * o / sqrt(mean(o^2) + eps) * silu(z) over Dv, in place
+//                         (or written token-major, with z read token-major).
 // In bf16 the first two are folded into the prefill's chunk-local kernel
 // (which holds every key row of its chunk anyway); they run as passes for
 // fp32 and where that kernel cannot write the unit rows over the raw ones.
@@ -90,7 +91,13 @@ __global__ __launch_bounds__(kRowThreads) void rms_gate_rows_kernel(const FusedP
   const int j = threadIdx.x & 15;
   if (row >= f.rows) return;
   T* o = static_cast<T*>(f.out) + row * f.Dv;
-  const T* z = static_cast<const T*>(f.z) + row * f.Dv;
+  // row = (b Hv + h) S + t; its token-major index is (b S + t) Hv + h
+  long tok_row = row;
+  if (f.out_tok) {
+    const long bh = row / f.S, t = row - bh * f.S, b = bh / f.Hv, h = bh - b * f.Hv;
+    tok_row = (b * f.S + t) * f.Hv + h;
+  }
+  const T* z = static_cast<const T*>(f.z) + (f.out_tok && f.z_token_major ? tok_row : row) * f.Dv;
   const bool valid = 8 * j < f.Dv;
   float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, zz[8], w[8];
   if (valid) {
@@ -105,11 +112,7 @@ __global__ __launch_bounds__(kRowThreads) void rms_gate_rows_kernel(const FusedP
   if (valid) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = w[i] * x[i] * rinv * (zz[i] * sigmoidf_(zz[i]));
-    T* dst = o;
-    if (f.out_tok) {  // row = (b Hv + h) S + t  ->  token-major [B, S, Hv Dv]
-      const long bh = row / f.S, t = row - bh * f.S, b = bh / f.Hv, h = bh - b * f.Hv;
-      dst = static_cast<T*>(f.out_tok) + ((b * f.S + t) * f.Hv + h) * f.Dv;
-    }
+    T* dst = f.out_tok ? static_cast<T*>(f.out_tok) + tok_row * f.Dv : o;  // token-major [B, S, Hv Dv]
     st8(dst + 8 * j, x);
   }
 }

@@ -109,6 +109,8 @@ struct FusedPost {
   // is only read
   void* out_tok;
   int S, Hv;
+  // with out_tok: z is token-major too, [B, S, Hv * Dv]
+  int z_token_major;
 };
 hipError_t launch_fused_pre(const FusedPre& f, int dtype, hipStream_t stream);
 hipError_t launch_fused_post(const FusedPost& f, int dtype, hipStream_t stream);
@@ -146,7 +148,7 @@ struct ConvSplitParams {
   void* q;                   // [B, Hk, S, Dk] bf16
   void* k;
   void* v;                   // [B, Hv, S, Dv] bf16
-  void* z_head;              // [B, Hv, S, Dv] bf16
+  void* z_head;              // [B, Hv, S, Dv] bf16; NULL: z is not moved
   // when not NULL: the a and b projections token-major, [2][B * S, Hv] bf16,
   // moved to a_head / b_head ([B, Hv, S] fp32)
   const void* ab_tok;

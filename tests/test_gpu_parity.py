@@ -458,6 +458,27 @@ def test_tkg_bh1024_workload_in_place(gpu_lib):
     assert torch.equal(s2, s) and torch.equal(y2, y)
 
 
+@pytest.mark.parametrize("B,Hv,dt", [(75, 20, "bf16"), (70, 30, "f32"), (33, 31, "bf16")],
+                         ids=["BH1500_bf16", "BH2100_f32", "BH1023_bf16"])
+def test_tkg_heads_over_several_launches(gpu_lib, B, Hv, dt):
+    """More heads than one round (1024) go out as several launches of an even
+    share each (1500 -> 2 x 750, 2100 -> 3 x 700; 1023 stays one launch): every
+    head, out-of-place and in-place, against the oracle."""
+    import torch
+    d = inputs.tkg_inputs(B, Hv, 128, 128, dtype=dt, seed=2200 + B * Hv)
+    args = [dev(x) for x in _tkg_args(d)]
+    y, s = gpu_lib.gdn_tkg(*args)
+    _sync()
+    ry, rs = _oracle_tkg(d)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert_close(host(s), rs, tol, 1, "state")
+    assert_close(host(y), ry, TOL_BF16, 1, "out")
+    st = args[-1].clone()
+    y2, s2 = gpu_lib.gdn_tkg(*args[:-1], st, state_out=st)
+    _sync()
+    assert torch.equal(s2, s) and torch.equal(y2, y)
+
+
 @pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-5])
 def test_tkg_rms_eps_sweep(gpu_lib, eps):
     d = inputs.tkg_inputs(2, 8, 128, 128, seed=2100)
