@@ -236,7 +236,10 @@ __device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
   return x;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// (the hardware reciprocal, within 1 ulp, instead of a correctly rounded
+// division: every use rounds the result or a product of it to bf16, or keeps
+// it far inside the fp32 tolerance)
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 // log(1 + e^x); above 20 the correction e^-x is below fp32 resolution of x.
 __device__ __forceinline__ float softplusf_(float x) { return x > 20.0f ? x : log1pf(__expf(x)); }
 
