@@ -293,6 +293,23 @@ __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitPa
                         (size_t)b * p.S * p.Hv;
     float* out = which ? p.b_head : p.a_head;
     const int nh = min(8, p.Hv - h0);
+    if (p.Hv % 8 == 0) {
+      // a token's 8 heads are one 16-byte piece
+      uint4 xr[kConvTok];  // all loads before the first store
+#pragma unroll
+      for (int u = 0; u < kConvTok; ++u)
+        xr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(src + (size_t)(t0 + u) * p.Hv + h0)
+                            : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < kConvTok; ++u) {
+        if (t0 + u >= t1) break;
+        float e[8];
+        unpack8(xr[u], e);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = e[q];
+      }
+      return;
+    }
     float x[8][kConvTok];  // all loads before the first store
 #pragma unroll
     for (int q = 0; q < 8; ++q)
