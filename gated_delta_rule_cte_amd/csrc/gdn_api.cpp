@@ -426,9 +426,9 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   cs.ab_tok = ab_gemm ? w + L.abtok : nullptr;
   cs.a_head = reinterpret_cast<float*>(w + L.a);
   cs.b_head = reinterpret_cast<float*>(w + L.b);
-  cs.mixed = w + L.mixed; cs.z_tok = w + L.ztok; cs.conv_weight = conv_weight; cs.conv_state = conv_state_in;
-  // z stays token-major: the output norm reads it there
-  cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v; cs.z_head = nullptr;
+  // (z stays token-major: the output norm reads it there)
+  cs.mixed = w + L.mixed; cs.conv_weight = conv_weight; cs.conv_state = conv_state_in;
+  cs.conv_state_out = conv_state_out; cs.q = w + L.q; cs.k = w + L.k; cs.v = w + L.v;
   cs.B = B; cs.S = S; cs.conv_dim = (int)conv_dim; cs.value_dim = (int)value_dim; cs.key_dim = (int)key_dim;
   cs.Hk = Hk; cs.Hv = Hv; cs.Dk = Dk; cs.Dv = Dv; cs.K_win = K_win;
   if ((e = gdn::launch_conv_split(cs, hs)) != hipSuccess) return launched(e);

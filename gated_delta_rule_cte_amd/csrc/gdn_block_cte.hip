@@ -11,8 +11,9 @@
 //                        reads, outputs staged through LDS for 16-byte stores;
 //   proj_narrow_kernel   the a and b projections (N = Hv), one wave per token;
 //   conv_split_kernel    conv + silu over the sequence, split into head-major
-//                        q, k, v (and z when asked), rounded to bf16;
-//   conv_window_kernel   the conv window after the last token.
+//                        q, k, v, rounded to bf16;
+//   conv_window_kernel   the conv window after the last token, and a, b moved
+//                        to head-major fp32.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -173,12 +174,13 @@ __global__ __launch_bounds__(kGThreads) void proj_narrow_kernel(const NarrowPara
 }
 
 // conv + silu over the sequence for 8 channels and a block of kConvTok tokens
-// (the window slides in registers, so each input row is read once), then the
-// split: channels [0, key_dim) -> q, [key_dim, 2 key_dim) -> k, the rest of
-// conv_dim -> v, all head-major bf16.  Further groups move z (8 channels) and,
-// when the narrow projections came from the GEMM, a and b (8 heads) from
-// token-major to head-major.
-constexpr int kConvTok = 16;
+// (the window slides in registers, so each input row is read once, plus the
+// K_win - 1 rows before the block), then the split: channels [0, key_dim) ->
+// q, [key_dim, 2 key_dim) -> k, the rest of conv_dim -> v, all head-major
+// bf16.  Eight tokens keep the kernel at 109 VGPRs, four waves per SIMD, so a
+// 4096-token sequence is two even rounds of workgroups (sixteen tokens took
+// 149 VGPRs, three waves per SIMD and 1.34 rounds: 44.7 against 33.9 us).
+constexpr int kConvTok = 8;
 
 __device__ __forceinline__ void unpack8(uint4 u, float* e) {
   const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
@@ -191,16 +193,15 @@ __device__ __forceinline__ void unpack8(uint4 u, float* e) {
 
 template <int KW>
 __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitParams p) {
-  const int gconv = p.conv_dim / 8, gz = p.z_head ? p.value_dim / 8 : 0, gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
-  const int ngrp = gconv + gz + gab;
+  const int gconv = p.conv_dim / 8;
   const int ntb = (p.S + kConvTok - 1) / kConvTok;
   const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
-  if (gid >= (long)p.B * ntb * ngrp) return;
-  const int grp = (int)(gid % ngrp);
-  const long btb = gid / ngrp;
+  if (gid >= (long)p.B * ntb * gconv) return;
+  const int grp = (int)(gid % gconv);
+  const long btb = gid / gconv;
   const int b = (int)(btb / ntb), t0 = (int)(btb - (long)b * ntb) * kConvTok;
   const int t1 = min(t0 + kConvTok, p.S);
-  if (grp < gconv) {
+  {
     const int c = 8 * grp;
     const __bf16* mixed = static_cast<const __bf16*>(p.mixed) + (size_t)b * p.S * p.conv_dim + c;
     const __bf16* st = static_cast<const __bf16*>(p.conv_state) + ((size_t)b * p.conv_dim + c) * p.K_win;
@@ -272,63 +273,52 @@ __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitPa
         if constexpr (KW >= 2) win[q][KW - 2] = e[q];  // the newest entry
       }
     }
-  } else if (grp < gconv + gz) {
-    const int cc = 8 * (grp - gconv), h = cc / p.Dv, d = cc - h * p.Dv;
-    const __bf16* zt = static_cast<const __bf16*>(p.z_tok) + (size_t)b * p.S * p.value_dim + cc;
-    __bf16* zh = static_cast<__bf16*>(p.z_head) + (((size_t)b * p.Hv + h) * p.S) * p.Dv + d;
-    // every row of the block requested before the first store (the source
-    // and destination types match, so the compiler may not reorder them)
-    uint4 zr[kConvTok];
-#pragma unroll
-    for (int u = 0; u < kConvTok; ++u)
-      zr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(zt + (size_t)(t0 + u) * p.value_dim)
-                          : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < kConvTok; ++u)
-      if (t0 + u < t1) *reinterpret_cast<uint4*>(zh + (size_t)(t0 + u) * p.Dv) = zr[u];
-  } else {
+  }
+}
+
+// a and b, [2][B*S, Hv] bf16 token-major -> [B, Hv, S] fp32: item id covers
+// 8 heads x kConvTok tokens of one of them
+__device__ __forceinline__ void ab_move(const ConvSplitParams& p, long id) {
+  const int gab = 2 * ((p.Hv + 7) / 8);
+  const int ntb = (p.S + kConvTok - 1) / kConvTok;
+  if (id >= (long)p.B * ntb * gab) return;
+  const int g = (int)(id % gab);
+  const long btb = id / gab;
+  const int b = (int)(btb / ntb), t0 = (int)(btb - (long)b * ntb) * kConvTok;
+  const int t1 = min(t0 + kConvTok, p.S);
+  {
     // a or b: 8 heads x the token block, [B*S, Hv] bf16 -> [B, Hv, S] fp32
-    const int g = grp - gconv - gz, which = g / ((p.Hv + 7) / 8), h0 = 8 * (g % ((p.Hv + 7) / 8));
+    const int which = g / ((p.Hv + 7) / 8), h0 = 8 * (g % ((p.Hv + 7) / 8));
     const __bf16* src = static_cast<const __bf16*>(p.ab_tok) + (size_t)which * p.B * p.S * p.Hv +
                         (size_t)b * p.S * p.Hv;
     float* out = which ? p.b_head : p.a_head;
-    const int nh = min(8, p.Hv - h0);
-    if (p.Hv % 8 == 0) {
-      // a token's 8 heads are one 16-byte piece
-      uint4 xr[kConvTok];  // all loads before the first store
+    // (a and b come token-major only when Hv % 8 == 0: a token's 8 heads are
+    // one 16-byte piece)
+    uint4 xr[kConvTok];  // all loads before the first store
 #pragma unroll
-      for (int u = 0; u < kConvTok; ++u)
-        xr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(src + (size_t)(t0 + u) * p.Hv + h0)
-                            : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < kConvTok; ++u)
+      xr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(src + (size_t)(t0 + u) * p.Hv + h0)
+                          : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-      for (int u = 0; u < kConvTok; ++u) {
-        if (t0 + u >= t1) break;
-        float e[8];
-        unpack8(xr[u], e);
+    for (int u = 0; u < kConvTok; ++u) {
+      if (t0 + u >= t1) break;
+      float e[8];
+      unpack8(xr[u], e);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = e[q];
-      }
-      return;
+      for (int q = 0; q < 8; ++q) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = e[q];
     }
-    float x[8][kConvTok];  // all loads before the first store
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int u = 0; u < kConvTok; ++u)
-        x[q][u] = (q < nh && t0 + u < t1) ? bf2f(src[(size_t)(t0 + u) * p.Hv + h0 + q]) : 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int u = 0; u < kConvTok; ++u)
-        if (q < nh && t0 + u < t1) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = x[q][u];
   }
 }
 
 // the window after the last token: the last K_win entries of [window | tokens]
-// (each thread reads its whole row before writing, so it may update in place)
+// (each thread reads its whole row before writing, so it may update in place);
+// the threads past B * conv_dim move a and b to head-major
 __global__ __launch_bounds__(kGThreads) void conv_window_kernel(const ConvSplitParams p) {
   const long gid = (long)blockIdx.x * kGThreads + threadIdx.x;
-  if (gid >= (long)p.B * p.conv_dim) return;
+  if (gid >= (long)p.B * p.conv_dim) {
+    if (p.ab_tok) ab_move(p, gid - (long)p.B * p.conv_dim);
+    return;
+  }
   const int b = (int)(gid / p.conv_dim), c = (int)(gid - (long)b * p.conv_dim);
   const __bf16* st = static_cast<const __bf16*>(p.conv_state) + gid * p.K_win;
   const __bf16* mixed = static_cast<const __bf16*>(p.mixed);
@@ -360,9 +350,8 @@ hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
-  const int gab = p.ab_tok ? 2 * ((p.Hv + 7) / 8) : 0;
-  const int gz = p.z_head ? p.value_dim / 8 : 0;
-  const long n = (long)p.B * ((p.S + kConvTok - 1) / kConvTok) * (p.conv_dim / 8 + gz + gab);
+  const long ntb = (p.S + kConvTok - 1) / kConvTok;
+  const long n = (long)p.B * ntb * (p.conv_dim / 8);
   if (n > 0) {
     const dim3 grid((unsigned)((n + kGThreads - 1) / kGThreads)), block(kGThreads);
     switch (p.K_win) {
@@ -378,7 +367,7 @@ hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long nw = (long)p.B * p.conv_dim;
+  const long nw = (long)p.B * p.conv_dim + (p.ab_tok ? (long)p.B * ntb * 2 * ((p.Hv + 7) / 8) : 0);
   if (nw > 0)
     hipLaunchKernelGGL(conv_window_kernel, dim3((unsigned)((nw + kGThreads - 1) / kGThreads)), dim3(kGThreads), 0,
                        stream, p);

@@ -141,16 +141,14 @@ struct NarrowParams {
 hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream);
 struct ConvSplitParams {
   const void* mixed;         // [B * S, conv_dim] bf16 (the q|k|v projection)
-  const void* z_tok;         // [B * S, value_dim] bf16
   const float* conv_weight;  // [conv_dim, K_win]
   const void* conv_state;    // [B, conv_dim, K_win] bf16, oldest first
   void* conv_state_out;      // same shape; may be conv_state
   void* q;                   // [B, Hk, S, Dk] bf16
   void* k;
   void* v;                   // [B, Hv, S, Dv] bf16
-  void* z_head;              // [B, Hv, S, Dv] bf16; NULL: z is not moved
-  // when not NULL: the a and b projections token-major, [2][B * S, Hv] bf16,
-  // moved to a_head / b_head ([B, Hv, S] fp32)
+  // when not NULL (Hv % 8 == 0 only): the a and b projections token-major,
+  // [2][B * S, Hv] bf16, moved to a_head / b_head ([B, Hv, S] fp32)
   const void* ab_tok;
   float* a_head;
   float* b_head;
