@@ -276,38 +276,24 @@ __global__ __launch_bounds__(kGThreads) void conv_split_kernel(const ConvSplitPa
   }
 }
 
-// a and b, [2][B*S, Hv] bf16 token-major -> [B, Hv, S] fp32: item id covers
-// 8 heads x kConvTok tokens of one of them
+// a and b, [2][B*S, Hv] bf16 token-major -> [B, Hv, S] fp32 (Hv % 8 == 0):
+// item id is one token's 8 heads, one 16-byte load; neighbouring items are
+// the next heads, then the next token, so a wave reads 1 KB in one piece and
+// each of its 8 stores writes 4 runs of 16 tokens
 __device__ __forceinline__ void ab_move(const ConvSplitParams& p, long id) {
-  const int gab = 2 * ((p.Hv + 7) / 8);
-  const int ntb = (p.S + kConvTok - 1) / kConvTok;
-  if (id >= (long)p.B * ntb * gab) return;
-  const int g = (int)(id % gab);
-  const long btb = id / gab;
-  const int b = (int)(btb / ntb), t0 = (int)(btb - (long)b * ntb) * kConvTok;
-  const int t1 = min(t0 + kConvTok, p.S);
-  {
-    // a or b: 8 heads x the token block, [B*S, Hv] bf16 -> [B, Hv, S] fp32
-    const int which = g / ((p.Hv + 7) / 8), h0 = 8 * (g % ((p.Hv + 7) / 8));
-    const __bf16* src = static_cast<const __bf16*>(p.ab_tok) + (size_t)which * p.B * p.S * p.Hv +
-                        (size_t)b * p.S * p.Hv;
-    float* out = which ? p.b_head : p.a_head;
-    // (a and b come token-major only when Hv % 8 == 0: a token's 8 heads are
-    // one 16-byte piece)
-    uint4 xr[kConvTok];  // all loads before the first store
+  const int g8 = p.Hv / 8;
+  if (id >= 2L * p.B * p.S * g8) return;
+  const int hg = (int)(id % g8);
+  const long tok = id / g8;  // (which * B + b) * S + t
+  const int which = (int)(tok / ((long)p.B * p.S));
+  const long bt = tok - (long)which * p.B * p.S;
+  const int b = (int)(bt / p.S), t = (int)(bt - (long)b * p.S);
+  const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const __bf16*>(p.ab_tok) + tok * p.Hv + 8 * hg);
+  float e[8];
+  unpack8(x, e);
+  float* out = (which ? p.b_head : p.a_head) + ((size_t)b * p.Hv + 8 * hg) * p.S + t;
 #pragma unroll
-    for (int u = 0; u < kConvTok; ++u)
-      xr[u] = t0 + u < t1 ? *reinterpret_cast<const uint4*>(src + (size_t)(t0 + u) * p.Hv + h0)
-                          : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < kConvTok; ++u) {
-      if (t0 + u >= t1) break;
-      float e[8];
-      unpack8(xr[u], e);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) out[((size_t)b * p.Hv + h0 + q) * p.S + t0 + u] = e[q];
-    }
-  }
+  for (int q = 0; q < 8; ++q) out[(size_t)q * p.S] = e[q];
 }
 
 // the window after the last token: the last K_win entries of [window | tokens]
@@ -367,7 +353,7 @@ hipError_t launch_conv_split(const ConvSplitParams& p, hipStream_t stream) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long nw = (long)p.B * p.conv_dim + (p.ab_tok ? (long)p.B * ntb * 2 * ((p.Hv + 7) / 8) : 0);
+  const long nw = (long)p.B * p.conv_dim + (p.ab_tok ? 2L * p.B * p.S * (p.Hv / 8) : 0);
   if (nw > 0)
     hipLaunchKernelGGL(conv_window_kernel, dim3((unsigned)((nw + kGThreads - 1) / kGThreads)), dim3(kGThreads), 0,
                        stream, p);
