@@ -12,8 +12,11 @@
  * Conventions shared by every entry point
  *   - Every pointer is a device pointer owned by the caller.  The library never
  *     allocates, frees or synchronises; it only launches kernels, in order, on
- *     `stream` (a hipStream_t; NULL is the null stream).  Launches are
- *     asynchronous: a kernel fault shows up at the caller's next synchronisation.
+ *     `stream` (a hipStream_t; NULL is the null stream).  (One exception:
+ *     gdn_block_cte runs its projections through hipBLASLt, whose handle is
+ *     created on the first call on each device and, with a plan per GEMM
+ *     shape, kept until the process ends.)  Launches are asynchronous: a
+ *     kernel fault shows up at the caller's next synchronisation.
  *   - Tensors are dense, row-major in the printed index order, and every
  *     pointer must be 16-byte aligned.
  *   - bf16 data is IEEE bfloat16 (upper half of an fp32), passed as void*.
@@ -276,6 +279,8 @@ size_t gdn_block_tkg_workspace_size(int B, int H, int num_k_heads,
  *   workspace    gdn_block_cte_workspace_size() bytes, 256-byte aligned,
  *                disjoint from every other argument: the projections, the
  *                head-major conv outputs, gates and the prefill scratch.
+ * The four projections are plain GEMMs and run on hipBLASLt (no workspace);
+ * a product the library declines runs on this library's own MFMA GEMM.
  * Stage boundaries are bf16 as in gdn_block_tkg; q, k are normalised to unit
  * rows (rounded to bf16) and scaled by Dk^-1/2 inside the prefill.
  * Constraints: those of gdn_block_tkg, plus S >= 0 and every buffer below
