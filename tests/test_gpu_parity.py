@@ -535,10 +535,13 @@ def _check_block(gpu_out, d):
 
 # H = 1024 / 4096 take the fully unrolled K loops; B = 70 spans two batch tiles
 # with a ragged second one; Hv = 8 takes the vector a|b tile; windows of 6 and
-# 8 take the generic conv epilogue up to the longest window the API accepts
+# 8 take the generic conv epilogue up to the longest window the API accepts;
+# B*Hv = 1120 and 1040 run the decode step as two launches (of 560 and 520
+# heads), the first at the model's head dims
 @pytest.mark.parametrize("case", [(3, 256, 2, 4, 32, 32, 4), (5, 384, 1, 2, 64, 48, 3), (2, 128, 2, 2, 16, 16, 1),
                                   (70, 1024, 2, 8, 32, 32, 4), (17, 4096, 1, 8, 16, 24, 2),
-                                  (4, 256, 2, 4, 32, 32, 8), (3, 128, 1, 2, 16, 24, 6)],
+                                  (4, 256, 2, 4, 32, 32, 8), (3, 128, 1, 2, 16, 24, 6),
+                                  (35, 2048, 16, 32, 128, 128, 4), (130, 256, 2, 8, 32, 32, 4)],
                          ids=lambda c: "B{}_H{}_Hk{}_Hv{}_Dk{}_Dv{}_W{}".format(*c))
 def test_block_small(gpu_lib, case):
     B, H, Hk, Hv, Dk, Dv, W = case
