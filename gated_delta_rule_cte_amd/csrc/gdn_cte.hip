@@ -1029,22 +1029,23 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
 // ===========================================================================
 // kernel 2, bf16: the same sequential pass with four data-mover waves
 // ===========================================================================
-// Eight waves per workgroup.  Waves 0-3 compute exactly as above (wave w owns
-// row block w of the chunk and the state blocks w + 4j) but issue no global
-// memory instruction inside the chunk loop; waves 4-7 only move data.  The
-// movers hold the next chunk's operands in their registers and write each
-// into LDS as soon as the compute phase that read the previous copy has passed
-// its barrier, then load the same operand of the chunk after that, so every
-// load has a whole chunk of time to arrive and the memory pipeline's issue
-// stalls fall on the movers:
-//   segment 1  compute: B          movers: P(c), K(c+1) -> LDS (K double
-//                                  buffered), outputs of c-1 -> HBM,
-//                                  load P(c+1), K(c+2)
+// Eight waves per workgroup.  Waves 0-3 compute as above (wave w owns row
+// block w of the chunk and the state blocks w + 4j, and forms scale Gam Q H
+// of its row block next to K H) but issue no global memory instruction inside
+// the chunk loop; waves 4-7 move data and finish the outputs.  The movers hold
+// two register sets of operands and write each into LDS as soon as the
+// compute phase that read the previous copy has passed its barrier, then load
+// the same operand of a later chunk, so every load has two chunks of time to
+// arrive and the memory pipeline's issue stalls fall on the movers:
+//   segment 1  compute: B          movers: K(c+1) -> LDS (K double buffered),
+//                                  load K(c+3); outputs of c-1 -> HBM
 //   barrier
-//   segment 2  compute: C          movers: Q, V, g scan, beta of c+1 -> LDS,
-//                                  load those of c+2
+//   segment 2  compute: C          movers: V, g scan, beta, Q of c+1 -> LDS,
+//                                  load those of c+3
 //   barrier
-//   segment 3  compute: D          movers: T(c+1) -> LDS, load T(c+2)
+//   segment 3  compute: D          movers: T(c+1) -> LDS, load T(c+3);
+//                                  O = scale Gam Q H + P U of chunk c (P in
+//                                  registers) -> LDS; load P(c+2)
 //   barrier
 // Only the lower 16x16 blocks of T and P are moved; their upper blocks are
 // zeroed once and never written again.
