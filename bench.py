@@ -55,6 +55,14 @@ OP_SOURCES = {
     "tkg": ["gdn_api.cpp", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
     "block": ["gdn_api.cpp", "gdn_block.hip", "gdn_tkg.hip", "gdn_device.h", "gdn_launch.h"],
 }
+CTE = dict(B=1, Hk=16, Hv=32, S=4096, Dk=128, Dv=128)
+TKG = dict(B=32, Hv=32, K=128, V=128)
+BLK = dict(B=64, H=2048, Hk=16, Hv=32, Dk=128, Dv=128, K_win=4)
+# the decode step runs in launches of at most one round (1024 heads), the
+# heads spread evenly over them
+TKG_ROUND = 1024
+BLOCK_TKG_LAUNCHES = -(-BLK["B"] * BLK["Hv"] // TKG_ROUND)
+BLOCK_TKG_GRID = -(-BLK["B"] * BLK["Hv"] // BLOCK_TKG_LAUNCHES) * 512
 # kernels of each entry point in the bench workloads: (name fragment, grid in
 # threads or None, launches per call).  The decode layer's decode-step launches
 # (two of 1024 heads) have the same name and grid as gdn_tkg's: record_traffic
@@ -63,15 +71,11 @@ OP_KERNELS = {
     "cte": [("cte_local1_kernel<128, 2, 1, 0, false>", 1 * 32 * 64 // 2 * 128, 1), ("cte_state_ws_kernel<128, 16,", None, 1)],
     "cte_long": [("cte_local1_kernel<128, 2, 1, 0, false>", 4 * 32 * 256 // 2 * 128, 1),
                  ("cte_state_ws_kernel<128, 64,", None, 1)],
-    "tkg": [("tkg_kernelIDF16bLi512E", 1024 * 512, 1)],       # the 512-thread form (mangled name)
-    "block": [("block_proj", None, 1), ("tkg_kernelIDF16bLi512E", 1024 * 512, 2)],
+    "tkg": [("tkg_kernelIDF16bLi512E", TKG["B"] * TKG["Hv"] * 512, 1)],   # the 512-thread form (mangled name)
+    "block": [("block_proj", None, 1), ("tkg_kernelIDF16bLi512E", BLOCK_TKG_GRID, BLOCK_TKG_LAUNCHES)],
 }
-BLOCK_TKG_LAUNCHES = 2
 COPY_CAL_BYTES = 512 << 20
 
-CTE = dict(B=1, Hk=16, Hv=32, S=4096, Dk=128, Dv=128)
-TKG = dict(B=32, Hv=32, K=128, V=128)
-BLK = dict(B=64, H=2048, Hk=16, Hv=32, Dk=128, Dv=128, K_win=4)
 NSETS = 4
 OP_REP = 16                    # calls per per-entry-point graph
 
