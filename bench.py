@@ -76,7 +76,13 @@ OP_KERNELS = {
 }
 COPY_CAL_BYTES = 512 << 20
 
-NSETS = 4
+NSETS = 4                      # input sets of the side benches
+# input sets per entry point in the main run, rotated so consecutive calls
+# touch more than the 256 MB Infinity Cache: the prefill and the decode step
+# use 8 (0.8 and 1.1 GB; with 4 they still ran 1.5 % and 3.5 % faster, part
+# of the sets staying cache-resident), the decode layer 4 (one set is
+# already 330 MB)
+SETS = dict(cte=8, tkg=8, block=4)
 OP_REP = 16                    # calls per per-entry-point graph
 
 
@@ -646,7 +652,7 @@ def main():
     if run_cte:
         d = inputs.workload_inputs("cte_bf16_b1_hk16_hv32_s4096_d128")
         base = {k: up(d[k]) for k in ("query", "key", "value", "g_log", "beta", "recurrent_state")}
-        for _ in range(NSETS):
+        for _ in range(SETS["cte"]):
             s = {k: v.clone() for k, v in base.items()}
             s["out"] = torch.empty((CTE["B"], CTE["Hv"], CTE["S"], CTE["Dv"]), dtype=torch.bfloat16, device=dev)
             cte_sets.append(s)
@@ -656,7 +662,7 @@ def main():
         d = inputs.workload_inputs("tkg_b32_hv32_d128")
         names = ("q", "k", "v", "b", "a", "A_log", "dt_bias", "z", "norm_weight", "state_in")
         base = {k: up(d[k]) for k in names}
-        for _ in range(NSETS):
+        for _ in range(SETS["tkg"]):
             s = {k: v.clone() for k, v in base.items()}
             s["state_out"] = torch.empty_like(s["state_in"])
             s["out"] = torch.empty((TKG["B"] * TKG["Hv"], TKG["V"]), dtype=torch.bfloat16, device=dev)
@@ -669,7 +675,7 @@ def main():
         base = {k: up(d[k]) for k in keys}
         ws_bytes = gdn.block_workspace_bytes(BLK["B"], BLK["H"], BLK["Hk"], BLK["Hv"], BLK["Dk"],
                                              BLK["Dv"], BLK["K_win"])
-        for _ in range(NSETS):
+        for _ in range(SETS["block"]):
             s = {k: v.clone() for k, v in base.items()}
             s["out"] = torch.empty((BLK["B"], 1, BLK["Hv"] * BLK["Dv"]), dtype=torch.bfloat16, device=dev)
             s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -717,28 +723,36 @@ def main():
                 long_single()
             torch.cuda.synchronize()
             del long_single
-        print(json.dumps({"eager_calls_per_op": args.eager * NSETS + NSETS, "ops": [n for n, _, _ in ops],
+        print(json.dumps({"eager_calls_per_op": {n: (args.eager + 1) * len(ss) for n, _, ss in ops},
+                          "ops": [n for n, _, _ in ops],
                           "long_single_calls": 0 if args.no_long else args.eager + 1}))
         return
 
     # -------------------------------------------------------------- graphs
     stream = torch.cuda.Stream()
-    step_graphs, op_graphs = [], {name: [] for name, _, _ in ops}
+    step_graphs, op_graphs, hot_graphs = [], {name: [] for name, _, _ in ops}, {}
+    n_steps = max(len(sets) for _, _, sets in ops)
     with torch.cuda.stream(stream):
-        for i in range(NSETS):
+        for i in range(n_steps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for _, fn, sets in ops:
-                    fn(sets[i])
+                    fn(sets[i % len(sets)])
             step_graphs.append(g)
         # per entry point: OP_REP calls in one graph (input sets in rotation),
-        # so the time per call carries no graph-launch gap
+        # so the time per call carries no graph-launch gap; and the same on
+        # one input set ("hot": partly cache-resident, reported apart)
         for name, fn, sets in ops:
             go = torch.cuda.CUDAGraph()
             with torch.cuda.graph(go, stream=stream):
                 for r in range(OP_REP):
-                    fn(sets[r % NSETS])
+                    fn(sets[r % len(sets)])
             op_graphs[name].append(go)
+            gh = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gh, stream=stream):
+                for r in range(OP_REP):
+                    fn(sets[0])
+            hot_graphs[name] = gh
     torch.cuda.synchronize()
 
     def timed(graphs, n):
@@ -754,16 +768,17 @@ def main():
     # warm-up steps, then exactly `steps` timed steps
     with torch.cuda.stream(stream):
         for j in range(args.warmup):
-            step_graphs[j % NSETS].replay()
+            step_graphs[j % len(step_graphs)].replay()
     torch.cuda.synchronize()
     ms_per_step = timed(step_graphs, args.steps)
     torch.cuda.synchronize()
 
-    per_op_ms = {}
+    per_op_ms, per_op_hot_ms = {}, {}
     for name, _, _ in ops:
         warm_replays(op_graphs[name][0], stream, torch, min_ms=30.0)
         reps = max(1, args.op_iters // OP_REP)
         per_op_ms[name] = timed(op_graphs[name], reps) / OP_REP
+        per_op_hot_ms[name] = timed([hot_graphs[name]], reps) / OP_REP
 
     # ---------------------------------------------------------- rooflines
     rooflines = {}
@@ -819,7 +834,7 @@ def main():
             "workload": ("gdn_cte bf16 B=1 Hk=16 Hv=32 S=4096 Dk=Dv=128 (in-place fp32 state) + "
                          "gdn_tkg BH=1024 K=V=128 + gdn_block_tkg B=64 H=2048 Hk=16 Hv=32 D=128 K_win=4"),
             "prefill_tokens_per_step": CTE["B"] * CTE["S"],
-            "input_sets_rotated": NSETS,
+            "input_sets_rotated": {n: len(ss) for n, _, ss in ops},
             "timing": ("HIP graphs replayed on one stream, HIP events; a step is one graph (all three "
                        "entry points), per-entry-point times come from graphs of 16 calls"),
         },
@@ -827,6 +842,7 @@ def main():
                                                       "block": "block_proj_kernel + tkg_kernel"}[dominant]),
         "cpu_baseline": cpu,
         "per_op_us": {k: v * 1e3 for k, v in per_op_ms.items()},
+        "per_op_hot_us": {k: v * 1e3 for k, v in per_op_hot_ms.items()},
         "rooflines": rooflines,
         "decode": ({"us_per_step": rooflines["tkg"]["us"], "GB_per_s": rooflines["tkg"]["achieved"],
                     "frac_of_8TBs": rooflines["tkg"]["frac"]} if run_tkg else None),
