@@ -1043,12 +1043,13 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
 //   segment 2  compute: C          movers: V, g scan, beta, Q of c+1 -> LDS,
 //                                  load those of c+3
 //   barrier
-//   segment 3  compute: D          movers: T(c+1) -> LDS, load T(c+3);
-//                                  O = scale Gam Q H + P U of chunk c (P in
-//                                  registers) -> LDS; load P(c+2)
+//   segment 3  compute: D          movers: O = scale Gam Q H + P U of chunk c
+//                                  (P in registers) -> LDS; load P(c+2)
 //   barrier
-// Only the lower 16x16 blocks of T and P are moved; their upper blocks are
-// zeroed once and never written again.
+// Only the lower 16x16 blocks of T and P are moved (the packed workspace
+// layout).  The compute waves load their own T fragments from it, one
+// chunk ahead: each 16-byte piece is used by one wave only, so staging T
+// through LDS would only add LDS writes, which run at half the read rate.
 // element index of (row t, column k) in a K tile: KSW = XOR-swizzled
 // 16-byte granules (granule k/8 of row t lives at granule (k/8) ^ swz(t)),
 // else a plain row pitch
@@ -1090,7 +1091,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   constexpr int kMovers = MW * kWave;                    // mover threads
   constexpr int kAll = (kWaves + MW) * kWave;
   constexpr int NKQ = C * (DK / 8) / kMovers;            // K or Q items per mover thread
-  constexpr int NTP = (kTriItems + kMovers - 1) / kMovers;
   constexpr int NVT = C * (DVT / 8);                     // V / O items
   constexpr int NVI = (NVT + kMovers - 1) / kMovers;
   constexpr uint32_t ES = 2;
@@ -1108,7 +1108,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   __shared__ __align__(16) T sK[2][C * LDKS];
   __shared__ __align__(16) T sQ[C * LDKS];  // Q of the chunk whose outputs the movers form
   __shared__ __align__(16) float sQH[kWaves * NVB * kWave * 4];  // scale Gam Q H, row block w, from wave w
-  __shared__ __align__(16) T sT[C * LDC];
   __shared__ __align__(16) T sV[C * LDV];
   __shared__ __align__(16) T sHt[DVT * LDK];
   __shared__ __align__(16) T sXt[DVT * LDC];
@@ -1143,8 +1142,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   T* og = static_cast<T*>(p.out) + (size_t)bh * S * Dv;
   float* stg = p.state + (size_t)bh * Dk * Dv;
 
-  // upper blocks of T read as zero for good
-  for (int i = tid; i < C * LDC / 2; i += kAll) reinterpret_cast<uint32_t*>(sT)[i] = 0u;
 
   f4 hacc[HPW];
   if (!mover) {
@@ -1164,23 +1161,13 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 
   // ---- mover state: loop-invariant offsets (bytes from the chunk start) and
   //      LDS element offsets of every item, and the in-flight registers
-  uint32_t vo_kq[NKQ], vo_tp[NTP], vo_v[NVI];
-  int lo_kq[NKQ], lo_tp[NTP], lo_v[NVI];
+  uint32_t vo_kq[NKQ], vo_v[NVI];
+  int lo_kq[NKQ], lo_v[NVI];
 #pragma unroll
   for (int i = 0; i < NKQ; ++i) {
     const int it = mt + kMovers * i, t = it / (DK / 8), c8 = 8 * (it % (DK / 8));
     vo_kq[i] = c8 < Dk ? (uint32_t)(t * Dk + c8) * ES : kOOB;
     lo_kq[i] = kidx<KSW, LDKS>(t, c8);
-  }
-#pragma unroll
-  for (int i = 0; i < NTP; ++i) {
-    const int it = mt + kMovers * i;
-    const int bi = it / 32;                                  // lower block, row-major order
-    const int rb = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
-    const int cb = bi - rb * (rb + 1) / 2;
-    const int row = 16 * rb + (it % 32) / 2, col = 16 * cb + 8 * (it % 2);
-    vo_tp[i] = it < kTriItems ? (uint32_t)it * 16u : kOOB;  // packed lower blocks
-    lo_tp[i] = it < kTriItems ? row * LDC + col : 0;
   }
 #pragma unroll
   for (int i = 0; i < NVI; ++i) {
@@ -1207,7 +1194,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   // two register sets: the set of chunk c holds P(c) and the Q, K, V, g,
   // beta, T of chunk c+1, so each load is issued two chunks before its use
   struct Regs {
-    V8 K[NKQ], Q[NKQ], Pf[KSTEPS], T[NTP], V[NVI];
+    V8 K[NKQ], Q[NKQ], Pf[KSTEPS], V[NVI];
     float g, b;
   };
   Regs rs0, rs1;
@@ -1233,11 +1220,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) m.Q[i] = V8::bload(r, vo_kq[i]);
   };
-  auto ld_t = [&](Regs& m, int c) {
-    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < c_end ? (uint32_t)kTriItems * 16u : 0u);
-#pragma unroll
-    for (int i = 0; i < NTP; ++i) m.T[i] = V8::bload(r, vo_tp[i]);
-  };
   auto ld_vg = [&](Regs& m, int c) {
     const auto rv = make_rsrc(vg + (size_t)c * C * Dv, rem_bytes(c, Dv));
 #pragma unroll
@@ -1251,7 +1233,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     ld_q(m, c + 1);
     ld_k(m, c + 1);
     ld_vg(m, c + 1);
-    ld_t(m, c + 1);
   };
   auto st_k = [&](const Regs& m, int slot) {
 #pragma unroll
@@ -1260,11 +1241,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   auto st_q = [&](const Regs& m) {
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) m.Q[i].store(sQ + lo_kq[i]);
-  };
-  auto st_tp = [&](T* dst, const V8* src) {
-#pragma unroll
-    for (int i = 0; i < NTP; ++i)
-      if (mt + kMovers * i < kTriItems) src[i].store(dst + lo_tp[i]);  // wave-uniform
   };
   auto st_vg = [&](const Regs& m) {
 #pragma unroll
@@ -1311,8 +1287,6 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     st_q(m);  // Q(c+1): every mover's Q(c) reads passed the barrier above
     ld_q(m, c + 3);
     __syncthreads();  // end of C
-    st_tp(sT, m.T);
-    ld_t(m, c + 3);
     f4 oacc[NVB];
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) oacc[vb] = *reinterpret_cast<const f4*>(sQH + ((mw * NVB + vb) * kWave + lane) * 4);
@@ -1325,15 +1299,13 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     // The two roles run separate code from here on, with the same barrier
     // sequence, so the load-to-use waits of each are counted on its own
     // instruction stream.
-    __syncthreads();  // T zeroed, initial state staged
+    __syncthreads();  // initial state staged
     ld_k(rs0, c_begin);
     ld_q(rs0, c_begin);
     ld_vg(rs0, c_begin);
-    ld_t(rs0, c_begin);
     st_k(rs0, c_begin & 1);
     st_q(rs0);
     st_vg(rs0);
-    st_tp(sT, rs0.T);
     ld_all(rs0, c_begin);
     ld_all(rs1, c_begin + 1);
     __syncthreads();  // chunk 0 staged
@@ -1347,13 +1319,28 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     return;
   }
 
-  __syncthreads();  // T zeroed, initial state staged
+  __syncthreads();  // initial state staged
   __syncthreads();  // chunk 0 staged
   const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
+  // T fragments of row block w straight from the packed workspace (lane
+  // (lr, lg) of k-step s: block j = 2 s + lg / 2, half lg % 2 of row lr, one
+  // 512-byte run per block); blocks above the diagonal read zero
+  uint32_t vo_tf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int j = 2 * s + (lg >> 1);
+    vo_tf[s] = j <= w ? (uint32_t)(32 * (w * (w + 1) / 2 + j) + 2 * lr + (lg & 1)) * 16u : kOOB;
+  }
+  auto ld_tf = [&](V8* tf, int c) {
+    const auto r = make_rsrc(ws_chunk<T>(p.ws, bh, NC, c), c < c_end ? (uint32_t)kTriItems * 16u : 0u);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) tf[s] = V8::bload(r, vo_tf[s]);
+  };
+  V8 tfa[KSTEPS], tfb[KSTEPS];
   // A padding chunk past the end (odd NC) is computed like any other: its
   // operands are zeros, exp(gam) = 1 and beta = 0, so the state is unchanged
   // and its outputs fall outside the range check.
-  auto compute_chunk = [&](int c) {
+  auto compute_chunk = [&](int c, const V8* tf, V8* tfn) {
     const T* sKc = sK[c & 1];
     float GC, dt[4];
     // ------------------------------------------------------------------- B
@@ -1401,7 +1388,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
         if (s < nks)
-          u = MM::mma(V8::load(sT + (16 * w + lr) * LDC + 32 * s + 8 * lg),
+          u = MM::mma(tf[s],
                       V8::load(sXt + (16 * vb + lr) * LDC + 32 * s + 8 * lg), u);
       const int off = (16 * vb + lr) * LDC + 16 * w + 4 * lg;
       store4<T>(sUt + off, u[0], u[1], u[2], u[3]);
@@ -1411,6 +1398,7 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
 
     // ------------------------------------------------------------------- D
     // H' = Gam_C H + K^T (d U)
+    ld_tf(tfn, c + 1);
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int hb = w + kWaves * j, kb = hb / NVB, vb = hb % NVB;
@@ -1425,9 +1413,10 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
     }
     __syncthreads();
   };
+  ld_tf(tfa, c_begin);
   for (int c = c_begin; c < c_end; c += 2) {
-    compute_chunk(c);
-    compute_chunk(c + 1);
+    compute_chunk(c, tfa, tfb);
+    compute_chunk(c + 1, tfb, tfa);
   }
 
 
