@@ -824,7 +824,10 @@ __global__ __launch_bounds__(kThreads) void cte_state_kernel(const CteParams p) 
     vo_k[i] = kc8[i] < Dk ? (uint32_t)(kt0[i] * Dk + kc8[i]) * ES : kOOB;
   }
   // T and P are only A operands of this wave's 16 rows: their fragments go
-  // straight into registers; upper 16x16 blocks read as zero
+  // straight into registers; upper 16x16 blocks read as zero.  The compiler
+  // may turn the s < nks guards below into EXEC masks, under which an MFMA
+  // still executes: the fragments past a guard are those zeros, so such a
+  // product adds nothing.
   const int nks = (16 * (w + 1) + 31) / 32;           // k-steps touching lower blocks
   uint32_t vo_t[KSTEPS];
 #pragma unroll
@@ -1187,6 +1190,8 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   for (int s = 0; s < KSTEPS; ++s) {
     // packed lower blocks: row 16 mw + lr, columns k8 .. + 7 are item
     // 32 tri(mw, k8 / 16) + 2 lr + (k8 / 8) % 2; upper blocks read as zero
+    // (so an MFMA past the s < mnks guard, which may compile to an EXEC mask
+    // under which it still executes, adds nothing)
     const int k8 = 32 * s + 8 * lg, bj = k8 >> 4;
     vo_pf[s] = (s < mnks && bj <= mw) ? (uint32_t)(32 * (mw * (mw + 1) / 2 + bj) + 2 * lr + ((k8 >> 3) & 1)) * 16u
                                        : kOOB;
@@ -1324,7 +1329,9 @@ __global__ __launch_bounds__((kWaves + MW) * kWave) void cte_state_ws_kernel(con
   const int nks = (16 * (w + 1) + 31) / 32;  // k-steps touching lower blocks
   // T fragments of row block w straight from the packed workspace (lane
   // (lr, lg) of k-step s: block j = 2 s + lg / 2, half lg % 2 of row lr, one
-  // 512-byte run per block); blocks above the diagonal read zero
+  // 512-byte run per block); blocks above the diagonal read zero, as the
+  // s < nks guard of U = T X relies on (it may compile to an EXEC mask, under
+  // which an MFMA still executes)
   uint32_t vo_tf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
