@@ -135,12 +135,37 @@ def block_bytes(B, H, Hk, Hv, Dk, Dv, K_win):
             + 2 * B * Hv * Dk * Dv * 4 + B * value_dim * 2 + 2 * Hv * 4 + Dv * 4)
 
 
+def code_only(text):
+    """C/C++ source without comments and blank space: what the compiler sees, so that an
+    edit to comments alone leaves a recorded traffic figure valid."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, escapes kept
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(" ".join(line.split()) for line in "".join(out).splitlines() if line.strip())
+
+
 def source_digest(op):
     import hashlib
     h = hashlib.sha256()
     for f in OP_SOURCES[op]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()
 
 
