@@ -395,11 +395,14 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
     return launched(e);
   }
   char* w = static_cast<char*>(workspace);
-  // The four projections are plain GEMMs and go to the vendor library; what
-  // it does not take runs in one launch of gemm_bf16_kernel (a and b join the
-  // GEMMs when their rows are whole 16-byte pieces, else they take one wave
-  // per token).
-  const bool ab_gemm = Hv % 8 == 0;
+  // The q|k|v and z projections are plain GEMMs and go to the vendor
+  // library; what it does not take runs in one launch of gemm_bf16_kernel.
+  // The narrow a and b projections (N = Hv) run as one MFMA kernel that
+  // reads hidden once and writes them head-major (Hv a multiple of 16 up to
+  // 64); other Hv join the GEMMs when their rows are whole 16-byte pieces,
+  // else they take one wave per token.
+  const bool ab_mfma = Hv % 16 == 0 && Hv <= 64;
+  const bool ab_gemm = !ab_mfma && Hv % 8 == 0;
   gdn::GemmParams gp{};
   gp.A = hidden; gp.M = (int)M; gp.K = H;
   auto add = [&](const void* Wm, void* Cm, int N) {
@@ -420,7 +423,8 @@ int gdn_block_cte(const void* hidden, const void* W_in_qkv, const void* W_in_z, 
   if (!ab_gemm) {
     gdn::NarrowParams na{hidden, W_in_a, W_in_b, reinterpret_cast<float*>(w + L.a),
                          reinterpret_cast<float*>(w + L.b), (int)M, Hv, H, S};
-    if ((e = gdn::launch_proj_narrow(na, hs)) != hipSuccess) return launched(e);
+    if ((e = ab_mfma ? gdn::launch_proj_ab(na, hs) : gdn::launch_proj_narrow(na, hs)) != hipSuccess)
+      return launched(e);
   }
   gdn::ConvSplitParams cs{};
   cs.ab_tok = ab_gemm ? w + L.abtok : nullptr;

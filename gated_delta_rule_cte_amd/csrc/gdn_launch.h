@@ -139,6 +139,9 @@ struct NarrowParams {
   int M, N, K, S;
 };
 hipError_t launch_proj_narrow(const NarrowParams& p, hipStream_t stream);
+// the same on MFMA; hipErrorNotSupported (nothing queued) unless N % 16 == 0,
+// N <= 64 and K % 32 == 0
+hipError_t launch_proj_ab(const NarrowParams& p, hipStream_t stream);
 struct ConvSplitParams {
   const void* mixed;         // [B * S, conv_dim] bf16 (the q|k|v projection)
   const float* conv_weight;  // [conv_dim, K_win]

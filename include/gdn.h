@@ -279,8 +279,11 @@ size_t gdn_block_tkg_workspace_size(int B, int H, int num_k_heads,
  *   workspace    gdn_block_cte_workspace_size() bytes, 256-byte aligned,
  *                disjoint from every other argument: the projections, the
  *                head-major conv outputs, gates and the prefill scratch.
- * The four projections are plain GEMMs and run on hipBLASLt (no workspace);
- * a product the library declines runs on this library's own MFMA GEMM.
+ * The q|k|v and z projections are plain GEMMs and run on hipBLASLt (no
+ * workspace); a product the library declines runs on this library's own MFMA
+ * GEMM.  The narrow a and b projections run on this library's own kernel
+ * (num_v_heads a multiple of 16 up to 64; other counts join the GEMMs or,
+ * when not a multiple of 8, a per-token kernel).
  * Stage boundaries are bf16 as in gdn_block_tkg; q, k are normalised to unit
  * rows (rounded to bf16) and scaled by Dk^-1/2 inside the prefill.
  * Constraints: those of gdn_block_tkg, plus S >= 0 and every buffer below

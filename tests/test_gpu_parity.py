@@ -148,6 +148,11 @@ BLOCK_CTE_CASES = [
     (1, 2, 128, 2, 2, 16, 24, 4, True, 0),      # fewer tokens than the conv window
     (1, 130, 128, 2, 2, 128, 128, 4, False, 1),  # full head dims, Neumann inverse
     (2, 70, 256, 4, 8, 32, 32, 4, True, 0),      # Hv % 8 == 0: a and b on the GEMM
+    # Hv % 16 == 0: a and b on their MFMA kernel (16, 48, 64 columns; token
+    # rows not a multiple of 16; H = 384 gives each wave three k-steps)
+    (2, 37, 256, 4, 16, 32, 32, 4, False, 0),
+    (1, 45, 128, 8, 48, 16, 16, 4, True, 0),
+    (3, 21, 384, 16, 64, 16, 16, 4, False, 0),
     # GQA groups of 3 and 4: the q, k rows are normalised by a separate pass
     # (several chunk-local waves read each key head, so none may overwrite it)
     (1, 90, 128, 1, 3, 32, 32, 4, False, 0),
