@@ -153,6 +153,7 @@ BLOCK_CTE_CASES = [
     (2, 37, 256, 4, 16, 32, 32, 4, False, 0),
     (1, 45, 128, 8, 48, 16, 16, 4, True, 0),
     (3, 21, 384, 16, 64, 16, 16, 4, False, 0),
+    (1, 3, 128, 2, 16, 16, 16, 2, True, 0),     # fewer token rows than one 16-row tile
     # GQA groups of 3 and 4: the q, k rows are normalised by a separate pass
     # (several chunk-local waves read each key head, so none may overwrite it)
     (1, 90, 128, 1, 3, 32, 32, 4, False, 0),
